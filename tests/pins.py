@@ -1,0 +1,376 @@
+"""Pins that tie the CPU oracle to things other than itself.
+
+Each pin raises AssertionError when the oracle disagrees with a value the pages print,
+a closed form, an invariant the pages state, a library routine, or brute force. They
+are plain functions so that tests/test_oracle_mutations.py can re-run all of them
+against an oracle with a planted mistake and check that some pin catches it.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+import workload as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _ref(w, **kw):
+    return oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                             q_kind=w.q_dtype, kv_kind=w.kv_dtype, k_scale=w.k_scale,
+                             v_scale=w.v_scale, **kw)
+
+
+def _torch_tables():
+    """Decoders built from torch's own dtype conversions (independent of oracle.storage)."""
+    import torch
+    e4m3 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    bits16 = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    return {
+        "fp8_e4m3": e4m3.to(torch.float64).numpy(),
+        "bf16": bits16.view(torch.bfloat16).to(torch.float64).numpy(),
+        "f16": bits16.view(torch.float16).to(torch.float64).numpy(),
+    }
+
+
+def _decode_lib(arr, kind, tabs):
+    if kind == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if kind == "f16":
+        return tabs["f16"][np.asarray(arr).view(np.uint16)]
+    return tabs[kind][np.asarray(arr)]
+
+
+def contiguous_cache(w, tabs=None):
+    """D10-style contiguous per-request cache [B, maxL, Hkv, d] in float64, built slot by slot.
+
+    Mirrors the pre-paging layout (one [max_seq_len, heads, head_dim] tensor per request)
+    from the intelliparadigm article, section 2.1. Decoding uses torch's conversions."""
+    tabs = tabs or _torch_tables()
+    B, maxL = w.batch, max(1, w.max_context_len)
+    Kc = np.zeros((B, maxL, w.num_kv_heads, w.head_dim))
+    Vc = np.zeros_like(Kc)
+    for b in range(B):
+        for t in range(int(w.context_lens[b])):
+            p = int(w.block_tables[b, t // w.block_size])
+            Kc[b, t] = _decode_lib(w.k_pool[p, t % w.block_size], w.kv_dtype, tabs) * w.k_scale
+            Vc[b, t] = _decode_lib(w.v_pool[p, t % w.block_size], w.kv_dtype, tabs) * w.v_scale
+    return Kc, Vc
+
+
+# ------------------------------------------------------------------ printed values
+
+def pin_kv_formula():
+    g = json.load(open(os.path.join(GOLDEN, "kv_formula.json")))
+    for c in g["cases"]:
+        per = oracle.kv_bytes_per_token(c["layers"], c["kv_heads"], c["head_dim"], c["bytes"])
+        assert per == c["per_token_bytes"], (c["model"], per)
+        req = oracle.kv_bytes_per_request(c["request_tokens"], c["layers"], c["kv_heads"],
+                                          c["head_dim"], c["bytes"])
+        assert req == c["request_bytes"], (c["model"], req)
+
+
+def pin_block_table_example():
+    g = json.load(open(os.path.join(GOLDEN, "block_table_example.json")))
+    bs, N = g["block_size"], g["pool_blocks"]
+    pool = np.zeros((N, bs, 1, 1), dtype=np.float32)
+    for blk in range(N):
+        for s in range(bs):
+            pool[blk, s, 0, 0] = 100 * blk + s
+    table = np.array(g["table"], dtype=np.int32)
+    L = max(t for t, _, _ in g["probe_tokens"]) + 1
+    seq = oracle.gather_sequence(pool, table, L, bs, N)
+    assert seq.shape[0] == L
+    for t, blk, slot in g["probe_tokens"]:
+        assert seq[t, 0, 0] == 100 * blk + slot, (t, seq[t, 0, 0])
+
+
+# ------------------------------------------------------------------ paging invariants
+
+def _small(kv="bf16", G=4, Hkv=2, d=64, lens=(1, 16, 17, 40, 95), seed=0, **kw):
+    return wl.custom(batch=len(lens), num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=d,
+                     kv_dtype=kv, context_lens=list(lens), seed=seed, **kw)
+
+
+def pin_permutation_invariance():
+    """Moving physical blocks (and rewriting the tables) leaves the output bitwise equal."""
+    w = _small()
+    base = _ref(w)
+    perm = np.random.default_rng(5).permutation(w.num_blocks)
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    t2 = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w.k_pool, w.v_pool, w.block_tables = k2, v2, t2
+    assert np.array_equal(_ref(w), base)
+
+
+def pin_contiguous_equality():
+    """Paged attention equals attention over the contiguous pre-paging cache (bitwise)."""
+    w = _small(kv="f16", G=2)
+    Kc, Vc = contiguous_cache(w)
+    out = _ref(w)
+    tabs = _torch_tables()
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        qb = _decode_lib(w.q[b], w.q_dtype, tabs)
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            o, _ = oracle.attend(qb[h], Kc[b, :L, g], Vc[b, :L, g], w.scale)
+            assert np.array_equal(o, out[b, h]), (b, h)
+
+
+def pin_nan_poison():
+    """NaN in every slot outside [0, L) changes nothing (masking by selection)."""
+    clean = _small(lens=(3, 16, 33, 47))
+    dirty = wl.poison_unused(_small(lens=(3, 16, 33, 47)))
+    a, b = _ref(clean), _ref(dirty)
+    assert np.isfinite(b).all()
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ softmax closed forms
+
+def pin_rows_sum_to_one():
+    w = _small()
+    _, probs = _ref(w, return_probs=True)
+    for (b, h), p in probs.items():
+        assert p.shape == (int(w.context_lens[b]),)
+        assert (p >= 0).all()
+        assert abs(p.sum() - 1.0) <= 1e-12
+
+
+def pin_single_token():
+    """L = 1: the only probability is 1, so the output is that token's V row exactly."""
+    w = _small(kv="f32", lens=(1, 1, 1))
+    out = _ref(w)
+    tabs = _torch_tables()
+    for b in range(w.batch):
+        v = _decode_lib(w.v_pool[w.block_tables[b, 0], 0], w.kv_dtype, tabs)
+        for h in range(w.num_q_heads):
+            assert np.array_equal(out[b, h], v[h // w.group]), (b, h)
+
+
+def pin_constant_keys():
+    """Equal keys for every token: uniform weights, output = mean of the V rows."""
+    w = _small(kv="f32", lens=(5, 16, 29))
+    Kc, Vc = contiguous_cache(w)
+    rng = np.random.default_rng(1)
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        row = rng.standard_normal((w.num_kv_heads, w.head_dim)).astype(np.float32)
+        for t in range(L):
+            w.k_pool[w.block_tables[b, t // 16], t % 16] = row
+    out = _ref(w)
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        for h in range(w.num_q_heads):
+            mean = Vc[b, :L, h // w.group].mean(axis=0)
+            assert np.max(np.abs(out[b, h] - mean)) <= 1e-12
+
+
+def pin_zero_query():
+    w = _small(kv="bf16", lens=(7, 40))
+    w.q[:] = 0
+    Kc, Vc = contiguous_cache(w)
+    out = _ref(w)
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        for h in range(w.num_q_heads):
+            assert np.max(np.abs(out[b, h] - Vc[b, :L, h // w.group].mean(axis=0))) <= 1e-12
+
+
+def pin_two_tokens():
+    """L = 2: out = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1."""
+    w = _small(kv="f32", lens=(2, 2), G=2)
+    Kc, Vc = contiguous_cache(w)
+    out = _ref(w)
+    q = w.q.astype(np.float64)
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            s0 = w.scale * math.fsum(q[b, h] * Kc[b, 0, g])
+            s1 = w.scale * math.fsum(q[b, h] * Kc[b, 1, g])
+            a0 = 1.0 / (1.0 + math.exp(s1 - s0))
+            a1 = 1.0 / (1.0 + math.exp(s0 - s1))
+            exp = a0 * Vc[b, 0, g] + a1 * Vc[b, 1, g]
+            assert np.max(np.abs(out[b, h] - exp)) <= 1e-12
+
+
+def pin_blockwise_merge():
+    """Blockwise softmax with per-block (m, l) merged by rescaling equals the global softmax.
+
+    Block statistics and the rescale merge as described in vLLM-PagedAttention与连续批处理
+    技术拆解, section 3.3, applied at 16-token blocks and again across 3-block partitions."""
+    w = _small(kv="bf16", lens=(16, 17, 100, 250), d=64)
+    Kc, Vc = contiguous_cache(w)
+    out = _ref(w)
+    tabs = _torch_tables()
+    bs, part = w.block_size, 3
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        qb = _decode_lib(w.q[b], w.q_dtype, tabs)
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            partials = []
+            for p0 in range(0, L, bs * part):
+                m, l, acc = -np.inf, 0.0, np.zeros(w.head_dim)
+                for j0 in range(p0, min(L, p0 + bs * part), bs):
+                    K = Kc[b, j0:min(L, j0 + bs), g]
+                    V = Vc[b, j0:min(L, j0 + bs), g]
+                    s = w.scale * (K @ qb[h])
+                    m_blk = s.max()
+                    m_new = max(m, m_blk)
+                    e = np.exp(s - m_new)
+                    alpha = math.exp(m - m_new) if m > -np.inf else 0.0
+                    l = l * alpha + e.sum()
+                    acc = acc * alpha + e @ V
+                    m = m_new
+                partials.append((m, l, acc))
+            M = max(p[0] for p in partials)
+            Ls = sum(p[1] * math.exp(p[0] - M) for p in partials)
+            O = sum(p[2] * math.exp(p[0] - M) for p in partials) / Ls
+            assert np.max(np.abs(O - out[b, h])) <= 1e-12, (b, h)
+
+
+# ------------------------------------------------------------------ brute force & library
+
+def _brute(w, tabs):
+    out = np.zeros((w.batch, w.num_q_heads, w.head_dim))
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        qb = _decode_lib(w.q[b], w.q_dtype, tabs).tolist()
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            ks, vs = [], []
+            for t in range(L):
+                blk, slot = int(w.block_tables[b][t // 16]), t % 16
+                ks.append([w.k_scale * x for x in
+                           _decode_lib(w.k_pool[blk][slot][g], w.kv_dtype, tabs).tolist()])
+                vs.append([w.v_scale * x for x in
+                           _decode_lib(w.v_pool[blk][slot][g], w.kv_dtype, tabs).tolist()])
+            s = [w.scale * math.fsum(qb[h][i] * k[i] for i in range(w.head_dim)) for k in ks]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = math.fsum(e)
+            for i in range(w.head_dim):
+                out[b, h, i] = math.fsum(e[t] * vs[t][i] for t in range(L)) / z
+    return out
+
+
+def pin_brute_force_scalar():
+    tabs = _torch_tables()
+    for w in (wl.make(1), _small(kv="fp8_e4m3", lens=(9, 33), d=64, Hkv=1, G=2)):
+        if w.kv_dtype == "fp8_e4m3":
+            w.k_scale, w.v_scale = 0.0123, 0.0456   # distinct scales catch swapped ones
+        ref = _ref(w)
+        bf = _brute(w, tabs)
+        assert np.max(np.abs(ref - bf)) <= 1e-12, w.name
+
+
+def pin_sdpa_library():
+    """torch's scaled_dot_product_attention in float64 on the contiguous cache."""
+    import torch
+    for w in (wl.make(1), _small(kv="bf16", G=4, Hkv=2, lens=(1, 30, 77))):
+        Kc, Vc = contiguous_cache(w)
+        out = _ref(w)
+        tabs = _torch_tables()
+        for b in range(w.batch):
+            L = int(w.context_lens[b])
+            q = torch.from_numpy(_decode_lib(w.q[b], w.q_dtype, tabs))[None, :, None, :]
+            k = torch.from_numpy(Kc[b, :L]).permute(1, 0, 2).repeat_interleave(w.group, 0)[None]
+            v = torch.from_numpy(Vc[b, :L]).permute(1, 0, 2).repeat_interleave(w.group, 0)[None]
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q.contiguous(), k.contiguous(), v.contiguous(), scale=w.scale)
+            assert np.max(np.abs(o[0, :, 0, :].numpy() - out[b])) <= 1e-12, (w.name, b)
+
+
+def pin_gqa_equals_repeated_mha():
+    """GQA with group G equals MHA whose kv heads are each repeated G times in order."""
+    w = _small(kv="bf16", G=4, Hkv=2)
+    ref = _ref(w)
+    G = w.group
+    w.k_pool = np.repeat(w.k_pool, G, axis=2)
+    w.v_pool = np.repeat(w.v_pool, G, axis=2)
+    w.num_kv_heads *= G
+    assert np.array_equal(_ref(w), ref)
+
+
+# ------------------------------------------------------------------ storage decoding
+
+def pin_storage_vs_torch():
+    tabs = _torch_tables()
+    codes8 = np.arange(256, dtype=np.uint8)
+    a, b = oracle.decode_storage(codes8, "fp8_e4m3"), tabs["fp8_e4m3"]
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+    assert oracle.e4m3_table()[0x7E] == 448.0 and oracle.e4m3_table()[0x01] == 2.0 ** -9
+    codes16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for kind, arr in (("bf16", codes16), ("f16", codes16.view(np.float16))):
+        a, b = oracle.decode_storage(arr, kind), tabs[kind]
+        assert np.array_equal(np.isnan(a), np.isnan(b)), kind
+        assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)]), kind
+
+
+# ------------------------------------------------------------------ cache write / copy
+
+def pin_cache_write_closed_form():
+    w = wl.make(1)
+    slots = w.slot_mapping.copy()
+    slots[1] = -1                                   # skipped entry
+    out = oracle.cache_write_ref(w.k_pool, w.k_new, slots)
+    touched = np.zeros(w.k_pool.shape[:2], dtype=bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        assert np.array_equal(out[s // 16, s % 16].view(np.uint32), w.k_new[t].view(np.uint32))
+        touched[s // 16, s % 16] = True
+    assert np.array_equal(out[~touched].view(np.uint32), w.k_pool[~touched].view(np.uint32))
+
+
+def pin_block_copy_closed_form():
+    w = _small(kv="bf16")
+    pairs = np.array([[w.block_tables[0, 0], w.num_blocks - 1],
+                      [w.block_tables[2, 1], w.num_blocks - 2]], dtype=np.int64)
+    out = oracle.block_copy_ref(w.k_pool, pairs)
+    for s, d in pairs:
+        assert np.array_equal(out[d], w.k_pool[s])
+    keep = np.setdiff1d(np.arange(w.num_blocks), pairs[:, 1])
+    assert np.array_equal(out[keep], w.k_pool[keep])
+
+
+def pin_cow_isolation():
+    """Copy-on-write keeps the shared prefix read-only and isolates every sample's tail."""
+    w = wl.make(4, batch=2)
+    k = oracle.block_copy_ref(w.k_pool, w.copy_pairs)
+    v = oracle.block_copy_ref(w.v_pool, w.copy_pairs)
+    fill = w.notes["partial_fill"]
+    for s, d in w.copy_pairs:                  # copies equal the original before any tail write
+        assert np.array_equal(k[d], w.k_pool[s]) and np.array_equal(v[d], w.v_pool[s])
+    k2 = oracle.cache_write_ref(k, w.k_new, w.slot_mapping)
+    v2 = oracle.cache_write_ref(v, w.v_new, w.slot_mapping)
+    nfull = w.notes["shared_full_blocks"]
+    shared = np.unique(w.block_tables[:, :nfull])
+    assert np.array_equal(k2[shared], w.k_pool[shared]) and np.array_equal(v2[shared], w.v_pool[shared])
+    # every sample's partial block keeps the prompt's first `fill` tokens, then its own tail
+    S = w.notes["samples"]
+    for b in range(w.batch):
+        blk = w.block_tables[b, nfull]
+        src = w.block_tables[(b // S) * S + S - 1, nfull]   # last sample keeps the original
+        assert np.array_equal(k2[blk, :fill], w.k_pool[src, :fill])
+        t0 = b * w.notes["tail"]
+        assert np.array_equal(k2[blk, fill:], w.k_new[t0:t0 + 16 - fill])
+    # every table entry is distinct within a row; only the full prefix blocks are shared
+    for b in range(w.batch):
+        assert np.unique(w.block_tables[b]).size == w.block_tables.shape[1]
+    counts = np.bincount(w.block_tables.reshape(-1), minlength=w.num_blocks)
+    assert set(np.unique(counts[counts > 0])) <= {1, S}
+    assert (counts == S).sum() == nfull * w.notes["prompts"]
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,115 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that some pin fails.
+
+Each mutation replaces one oracle function with a wrong variant for the duration of
+the test; the pin suite must raise for every one of them, otherwise the pins would not
+be able to tell a broken oracle from a correct one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as att
+import oracle.cache_ops as cops
+import oracle.storage as st
+from pins import ALL_PINS
+
+
+def _fails(pins=ALL_PINS):
+    failed = []
+    for p in pins:
+        try:
+            p()
+        except Exception as e:          # AssertionError, or a shape error the mistake causes
+            failed.append((p.__name__, type(e).__name__))
+    return failed
+
+
+def _interleaved_gqa(h, group):
+    return h % 2                        # kv heads interleaved instead of contiguous groups
+
+
+def _no_truncation(pool, table_row, L, block_size, num_blocks):
+    nb = (L + block_size - 1) // block_size
+    ids = np.asarray(table_row[:nb], dtype=np.int64)
+    return pool[ids].reshape((nb * block_size,) + pool.shape[2:])   # attends padded slots
+
+
+def _shifted_table(pool, table_row, L, block_size, num_blocks):
+    nb = (L + block_size - 1) // block_size
+    ids = np.asarray(np.roll(table_row[:nb], 1), dtype=np.int64)   # logical j -> table[j-1]
+    return pool[ids].reshape((nb * block_size,) + pool.shape[2:])[:L]
+
+
+def _unnormalised(qv, K, V, scale):
+    s = scale * (K @ qv)
+    p = np.exp(s - s.max())
+    return p @ V, p
+
+
+def _scale_squared(qv, K, V, scale):
+    s = scale * scale * (K @ qv)
+    p = np.exp(s - s.max())
+    p = p / p.sum()
+    return p @ V, p
+
+
+def _linear_weights(qv, K, V, scale):
+    s = scale * (K @ qv)
+    p = s - s.min() + 1e-3
+    p = p / p.sum()
+    return p @ V, p
+
+
+def _bias8_table():
+    t = np.empty(256)
+    for code in range(256):
+        sign = -1.0 if code >> 7 else 1.0
+        e, m = (code >> 3) & 15, code & 7
+        t[code] = np.nan if (e == 15 and m == 7) else (
+            sign * m / 8 * 2.0 ** -7 if e == 0 else sign * (1 + m / 8) * 2.0 ** (e - 8))
+    return t
+
+
+def _bf16_low_half(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def _write_swapped(pool, new, slot_mapping):
+    out = pool.copy()
+    for t, s in enumerate(slot_mapping):
+        if s >= 0:
+            out[s % pool.shape[0], (s // pool.shape[0]) % pool.shape[1]] = new[t]
+    return out
+
+
+def _copy_reversed(pool, pairs):
+    out = pool.copy()
+    for s, d in np.asarray(pairs).reshape(-1, 2):
+        out[s] = pool[d]
+    return out
+
+
+MUTATIONS = {
+    "gqa_interleaved": (att, "kv_head_of", _interleaved_gqa),
+    "no_length_mask": (att, "gather_sequence", _no_truncation),
+    "table_off_by_one": (att, "gather_sequence", _shifted_table),
+    "softmax_unnormalised": (att, "attend", _unnormalised),
+    "scale_squared": (att, "attend", _scale_squared),
+    "linear_not_exp": (att, "attend", _linear_weights),
+    "e4m3_bias_8": (st, "e4m3_table", _bias8_table),
+    "bf16_low_half": (st, "bf16_bits_to_f64", _bf16_low_half),
+    "slot_index_swapped": (cops, "cache_write_ref", _write_swapped),
+    "copy_direction_reversed": (cops, "block_copy_ref", _copy_reversed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    mod, attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    # the package re-exports some names; patch those too so every caller sees the mistake
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    if mod is st and attr == "e4m3_table":
+        monkeypatch.setattr(st, "_E4M3_CACHE", None)
+    assert _fails(), f"no pin caught the planted mistake {name}"
