@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Paged decode-attention benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: copy-on-write block copies
+(configuration 4 only), the slot write of the step's new tokens (configurations 1, 3,
+4), then decode attention over every sequence (split-KV partitions + merge). Inputs
+are synthetic and seeded (workload.py) and resident in HBM before timing starts.
+
+The pool is replicated R times (default 3) and step i uses replica i % R, so that a
+step never finds the previous step's KV in the 256 MB Infinity Cache or the L2s.
+
+Output: one JSON line on stdout. `value` is KV-read GB/s over the whole step
+(sum_b L_b * 2 * Hkv * d * bytes / step time); `tokens_per_s` is sequences (one new
+token each) per second for this one attention layer. `roofline` describes the decode
+launch (main + merge kernels), timed with HIP events on the stream it runs on.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode KV-read GB/s (% HBM peak) & tokens/s, 8B GQA bf16 layer"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_367_amd", "csrc", "pa_decode.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(config_name: str):
+    """HBM bytes per decode launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not h or h.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{re.escape(config_name)}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(w, gpu_out, k_after, v_after, budget_s: float):
+    """Time the oracle on sequences in a seeded order until ~budget_s of CPU work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:  # noqa: BLE001 - reporting only
+        threads = None
+    order = np.random.default_rng(0).permutation(w.batch)
+    done, t0 = [], time.perf_counter()
+    refs = []
+    for b in order:
+        refs.append(oracle.decode_ref(w.q, k_after, v_after, w.block_tables, w.context_lens,
+                                      w.scale, q_kind=w.q_dtype, kv_kind=w.kv_dtype,
+                                      k_scale=w.k_scale, v_scale=w.v_scale, seqs=[int(b)]))
+        done.append(int(b))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    L = w.context_lens[done].astype(np.int64)
+    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_dim * {"f32": 4, "f16": 2, "bf16": 2,
+                                                           "fp8_e4m3": 1}[w.kv_dtype]
+    err = float(np.max(np.abs(gpu_out[done] - np.concatenate(refs, 0))))
+    return {
+        "value": kv / dt / 1e9, "unit": "GB/s", "tokens_per_s": len(done) / dt,
+        "cores": threads, "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": f"{len(done)} of {w.batch} sequences ({int(L.sum())} tokens), fp64 numpy, "
+                  f"{dt:.1f} s",
+        "sample_max_abs_err_vs_gpu": err,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = Llama-3-8B GQA bf16)")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per split-KV partition (default: the workload's, else the library's)")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported. Each GPU would own a disjoint set of "
+              "sequences and pool blocks, so no multi-GPU figure is produced.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_367_amd as pa
+    import workload as wl
+
+    pa.load_library()          # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    log(f"building workload {args.config}")
+    t0 = time.perf_counter()
+    w = wl.make(args.config)
+    log(f"workload {w.name}: B={w.batch} tokens={w.total_tokens} kv_bytes={w.kv_bytes} "
+        f"pool_blocks={w.num_blocks} ({time.perf_counter() - t0:.1f} s)")
+    part = args.partition_size if args.partition_size is not None else w.partition_size
+
+    def dev(a, kind=None):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if kind == "bf16" \
+            else torch.from_numpy(a)
+        return t.cuda()
+
+    q = dev(w.q, w.q_dtype)
+    tables, lens = dev(w.block_tables), dev(w.context_lens)
+    R = max(1, args.replicas)
+    ks = [dev(w.k_pool, w.kv_dtype) for _ in range(R)]
+    vs = [dev(w.v_pool, w.kv_dtype) for _ in range(R)]
+    slots = dev(w.slot_mapping) if w.slot_mapping is not None else None
+    k_new = dev(w.k_new, w.kv_dtype) if w.k_new is not None else None
+    v_new = dev(w.v_new, w.kv_dtype) if w.v_new is not None else None
+    pairs = dev(w.copy_pairs) if w.copy_pairs is not None else None
+    out_dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.out_dtype]
+    out = torch.empty(tuple(w.q.shape), dtype=out_dtype, device="cuda")
+    desc = pa.binding.make_desc(q, ks[0], tables, out, part)
+    ws_bytes = pa.pa_decode_workspace_bytes(desc, w.max_context_len)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    resolved_part = pa.pa_decode_partition_size(desc, w.max_context_len)
+    torch.cuda.synchronize()
+    log(f"resident: {R} pool replicas, workspace {ws_bytes} B, partition {resolved_part}")
+
+    n_ev = args.steps
+    dec0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    dec1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i, timed):
+        r = i % R
+        if pairs is not None:
+            pa.pa_block_copy(ks[r], vs[r], pairs)
+        if slots is not None:
+            pa.pa_cache_write(ks[r], vs[r], k_new, v_new, slots)
+        if timed:
+            dec0[i].record()
+        pa.pa_decode(out, q, ks[r], vs[r], tables, lens, w.max_context_len, w.scale, w.k_scale,
+                     w.v_scale, workspace=ws, partition_size=part)
+        if timed:
+            dec1[i].record()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in zip(dec0, dec1)]
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step, decode launch avg {dec_avg:.4f} ms "
+        f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f})")
+
+    gbs = w.kv_bytes / (ms * 1e-3) / 1e9
+    achieved = w.kv_bytes / (dec_avg * 1e-3) / 1e9
+    record = {
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[w.kv_dtype],
+        "data": "synthetic (seeded, workload.py)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+            "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "accumulate": "f32",
+            "context_tokens": w.total_tokens, "max_context_len": w.max_context_len,
+            "kv_bytes_per_step": w.kv_bytes, "partition_size": resolved_part,
+            "pool_replicas": R, "seed": w.seed,
+        },
+        "tokens_per_s": w.batch / (ms * 1e-3),
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "roofline": {
+            "kernel": "pa_decode (decode_kernel + merge_kernel)", "bound": "hbm",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
+            "launch_ms": dec_avg, "algorithmic_bytes_per_launch": w.kv_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: applying the step's writes to host pools")
+        k_after, v_after = w.k_pool, w.v_pool
+        if w.copy_pairs is not None:
+            k_after = oracle.block_copy_ref(k_after, w.copy_pairs)
+            v_after = oracle.block_copy_ref(v_after, w.copy_pairs)
+        if w.slot_mapping is not None:
+            k_after = oracle.cache_write_ref(k_after, w.k_new, w.slot_mapping)
+            v_after = oracle.cache_write_ref(v_after, w.v_new, w.slot_mapping)
+        gpu_out = out.to(torch.float64).cpu().numpy()
+        log(f"cpu baseline: timing the oracle (~{args.cpu_budget_s:.0f} s)")
+        record["cpu_baseline"] = cpu_baseline(w, gpu_out, k_after, v_after, args.cpu_budget_s)
+        log(f"cpu baseline: {record['cpu_baseline']['sample']}")
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

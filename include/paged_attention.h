@@ -1,0 +1,159 @@
+/*
+ * paged_attention.h - C ABI of the paged decode-attention library (libpa.so, gfx950).
+ *
+ * The library implements the data-parallel hot path of PagedAttention on one MI355X:
+ * decode-phase attention over a KV cache cut into fixed 16-token blocks that sit
+ * anywhere in a physical pool, the slot write that stores a new token's K/V, and the
+ * block copy behind copy-on-write of shared blocks.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller (allocated with
+ *     hipMalloc, or by a framework). The library allocates nothing, frees nothing and
+ *     keeps no pointer after a call returns. Scalars and the descriptor are host values
+ *     read during the call only.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream). Buffers must stay valid until that stream has executed the work.
+ *   - Arrays are dense, row-major, no padding between rows.
+ *   - Every argument the host can see is checked before anything is launched; a bad
+ *     argument returns an error code and launches nothing. Errors are return codes
+ *     only. Contents of device arrays (table entries, lengths, slots, pairs) are the
+ *     caller's contract: kernels never read or write outside the pool for out-of-range
+ *     entries (they skip them), but the result for such entries is unspecified.
+ *   - No global mutable state: calls are thread-safe.
+ */
+#ifndef PAGED_ATTENTION_H
+#define PAGED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element encodings. PA_FP8_E4M3 is OCP E4M3FN (bias 7, max 448, no infinities), the
+ * format behind "--kv-cache-dtype fp8" (vLLM-PagedAttention与连续批处理技术拆解,
+ * section 五, flag table and the FP8 KV-cache note). */
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3
+} pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                              */
+  PA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or sizes disagree */
+  PA_ERR_DTYPE = -3,       /* unknown dtype code                                       */
+  PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim, group, dtype combo)   */
+  PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                         */
+  PA_ERR_HIP = -7          /* the HIP runtime reported an error at launch              */
+} pa_status_t;
+
+/* Shape of one decode call.
+ *   batch               B, sequences (one query token each); 0 is allowed (no-op)
+ *   num_q_heads         Hq
+ *   num_kv_heads        Hkv; Hq % Hkv == 0; group G = Hq / Hkv in {1, 2, 4, 8}
+ *   head_dim            d in {64, 128}
+ *   block_size          tokens per block; must be 16
+ *   num_blocks          N, physical blocks in each pool
+ *   max_blocks_per_seq  width of the block table (maxb)
+ *   q_dtype, kv_dtype, out_dtype   pa_dtype_t codes; supported (q, kv, out):
+ *                       (F32,F32,F32) (F16,F16,F16|F32) (BF16,BF16,BF16|F32)
+ *                       (BF16,FP8_E4M3,BF16|F32)
+ *   partition_size      tokens per split-KV partition; 0 = library default;
+ *                       otherwise a multiple of 16 in [16, 4096] */
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t q_dtype;
+  int32_t kv_dtype;
+  int32_t out_dtype;
+  int32_t partition_size;
+} pa_decode_desc_t;
+
+/* Version of this ABI (1). */
+int32_t pa_abi_version(void);
+
+/* Human-readable text for a pa_status_t value; never NULL, static storage. */
+const char* pa_status_string(int32_t status);
+
+/* Partition size (tokens) pa_decode will use for this descriptor and max_context_len,
+ * or a negative pa_status_t if the descriptor is invalid. */
+int32_t pa_decode_partition_size(const pa_decode_desc_t* desc, int32_t max_context_len);
+
+/* Bytes of device workspace pa_decode needs (0 when every sequence fits in one
+ * partition). The workspace holds, for each (sequence, query head, partition), the
+ * partition's running max m (log2 domain), normaliser l and unnormalised output
+ * acc[d], all fp32. Returns 0 for an invalid descriptor. */
+size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_context_len);
+
+/* Decode attention over the paged KV cache.
+ *
+ * Defines: for each sequence b and query head h, with L = context_lens[b],
+ * g = h / G and token t stored at k_pool[block_tables[b][t / 16]][t % 16][g][:],
+ *   s_t = scale * k_scale * dot(q[b][h], K_t)          t < L
+ *   out[b][h] = v_scale * sum_t softmax(s)_t * V_t
+ * computed blockwise: every 16-token block contributes its local max and normaliser,
+ * merged by FlashAttention-style rescaling, which equals the global softmax
+ * (vLLM-PagedAttention与连续批处理技术拆解, sections 3.1-3.3; block-table lookup as in
+ * the paged_attention sketch of "AI vLLM：PagedAttention不够用了之后"). Sequences
+ * longer than one partition are split; each partition's (m, l, acc) is merged by a
+ * second kernel with the same rescaling. Positions >= L are never attended, whatever
+ * the slots hold (NaN included). L == 0 gives a zero output.
+ *
+ * Arguments (device pointers unless noted):
+ *   out            [B, Hq, d] out_dtype, written
+ *   q              [B, Hq, d] q_dtype
+ *   k_pool, v_pool [N, 16, Hkv, d] kv_dtype (separate K and V pools)
+ *   block_tables   [B, maxb] int32; entries past ceil(L/16) are ignored (-1 by convention)
+ *   context_lens   [B] int32, each in [0, min(maxb*16, max_context_len)]
+ *   max_context_len host int >= every context_lens[b]; sizes the launch (no device sync)
+ *   scale          host float, usually 1/sqrt(d)
+ *   k_scale, v_scale host floats, dequantisation scales for fp8 pools (use 1 otherwise)
+ *   workspace, workspace_bytes  device scratch of at least pa_decode_workspace_bytes();
+ *                  may be NULL when that is 0; contents need no initialisation
+ * All pointers must be 16-byte aligned. */
+pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
+                      const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, float k_scale, float v_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Slot write of new tokens (reshape_and_cache): a generated token occupies one slot
+ * (vLLM-PagedAttention与连续批处理技术拆解, section 3.1). For each t < num_tokens with
+ * slot_mapping[t] = s >= 0:
+ *   k_pool[s / block_size][s % block_size][:][:] = k_new[t][:][:]   (and V likewise)
+ * a bit-exact copy in the pool's encoding. s < 0 skips the token; slots must be
+ * distinct and < num_blocks * block_size (out-of-range slots are skipped).
+ *   k_pool, v_pool [N, block_size, Hkv, d]; k_new, v_new [T, Hkv, d]; slot_mapping [T]
+ *   int64. Hkv * d * bytes(kv_dtype) must be a multiple of 16. */
+pa_status_t pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t kv_dtype, void* stream);
+
+/* Copy-on-write block copy: a shared block is read-only and a sequence that must write
+ * into it copies it first (vLLM-PagedAttention与连续批处理技术拆解, section 3.4). For
+ * each pair p: k_pool[dst_p] = k_pool[src_p] and v_pool[dst_p] = v_pool[src_p], whole
+ * blocks (block_size x Hkv x d), bit-exact.
+ *   src_dst_pairs [P, 2] int64 (src, dst). Destinations must be distinct and no
+ *   destination may be a source in the same call; pairs with an id outside [0, N) are
+ *   skipped. */
+pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
+                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H */

@@ -1,0 +1,231 @@
+// pa_api.cpp - the C ABI: argument validation, launch configuration, error codes.
+//
+// Every check that the host can make happens here, before anything is launched; a bad
+// argument returns its pa_status_t and touches neither the GPU nor the HIP runtime.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/paged_attention.h"
+#include "pa_launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_dtype(int32_t d) { return d >= PA_F32 && d <= PA_FP8_E4M3; }
+
+int dtype_bytes(int32_t d) {
+  switch (d) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    default: return 1;
+  }
+}
+
+bool supported_combo(int32_t q, int32_t kv, int32_t out) {
+  if (q == PA_F32 && kv == PA_F32) return out == PA_F32;
+  if (q == PA_F16 && kv == PA_F16) return out == PA_F16 || out == PA_F32;
+  if (q == PA_BF16 && (kv == PA_BF16 || kv == PA_FP8_E4M3))
+    return out == PA_BF16 || out == PA_F32;
+  return false;
+}
+
+pa_status_t check_desc(const pa_decode_desc_t* d, int32_t max_context_len) {
+  if (!d) return PA_ERR_NULL;
+  if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->block_size <= 0 || d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 ||
+      max_context_len < 0 || d->partition_size < 0)
+    return PA_ERR_SHAPE;
+  if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype) || !valid_dtype(d->out_dtype))
+    return PA_ERR_DTYPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int group = d->num_q_heads / d->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (d->block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!supported_combo(d->q_dtype, d->kv_dtype, d->out_dtype)) return PA_ERR_UNSUPPORTED;
+  if (d->partition_size != 0 &&
+      (d->partition_size % pa::kBlockTokens != 0 || d->partition_size > pa::kMaxPartitionTokens))
+    return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)d->max_blocks_per_seq * pa::kBlockTokens)
+    return PA_ERR_SHAPE;
+  if (d->batch > 65535 || d->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;  // grid y/z
+  // byte offsets inside one physical block must fit 32 bits; pool size must fit size_t
+  const int64_t block_bytes =
+      (int64_t)pa::kBlockTokens * d->num_kv_heads * d->head_dim * dtype_bytes(d->kv_dtype);
+  if (block_bytes > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int32_t resolve_partition(const pa_decode_desc_t* d) {
+  return d->partition_size ? d->partition_size : pa::kDefaultPartitionTokens;
+}
+
+int32_t max_parts_for(const pa_decode_desc_t* d, int32_t max_context_len) {
+  const int32_t part = resolve_partition(d);
+  const int32_t n = (max_context_len + part - 1) / part;
+  return n > 0 ? n : 1;
+}
+
+size_t ws_acc_bytes(const pa_decode_desc_t* d, int32_t max_parts) {
+  return (size_t)d->batch * d->num_q_heads * max_parts * d->head_dim * sizeof(float);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return 1; }
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case PA_ERR_DTYPE: return "unknown dtype code";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t pa_decode_partition_size(const pa_decode_desc_t* desc, int32_t max_context_len) {
+  const pa_status_t st = check_desc(desc, max_context_len);
+  if (st != PA_OK) return st;
+  return resolve_partition(desc);
+}
+
+size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_context_len) {
+  if (check_desc(desc, max_context_len) != PA_OK) return 0;
+  const int32_t mp = max_parts_for(desc, max_context_len);
+  if (mp <= 1 || desc->batch == 0) return 0;
+  const size_t acc = align_up(ws_acc_bytes(desc, mp), 256);
+  const size_t ml = (size_t)desc->batch * desc->num_q_heads * mp * 2 * sizeof(float);
+  return acc + ml;
+}
+
+pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
+                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t max_context_len, float scale,
+                      float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  pa_status_t st = check_desc(desc, max_context_len);
+  if (st != PA_OK) return st;
+  if (desc->batch == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_SHAPE;
+  const size_t need = pa_decode_workspace_bytes(desc, max_context_len);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  }
+  const int32_t part = resolve_partition(desc);
+  const int32_t mp = max_parts_for(desc, max_context_len);
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            align_up(ws_acc_bytes(desc, mp), 256))
+                 : nullptr;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks_per_seq = desc->max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.part_blocks = part / pa::kBlockTokens;
+  a.max_parts = mp;
+  a.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int group = desc->num_q_heads / desc->num_kv_heads;
+  if (pa::launch_decode(desc->q_dtype, desc->kv_dtype, desc->out_dtype, desc->head_dim, group, a,
+                        desc->batch, s) != hipSuccess)
+    return PA_ERR_HIP;
+  if (mp > 1) {
+    pa::MergeArgs m;
+    m.out = out;
+    m.context_lens = context_lens;
+    m.ws_acc = a.ws_acc;
+    m.ws_ml = a.ws_ml;
+    m.num_q_heads = desc->num_q_heads;
+    m.max_blocks_per_seq = desc->max_blocks_per_seq;
+    m.max_context_len = max_context_len;
+    m.part_blocks = a.part_blocks;
+    m.max_parts = mp;
+    m.v_scale = v_scale;
+    if (pa::launch_merge(desc->out_dtype, desc->head_dim, m, desc->batch, s) != hipSuccess)
+      return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+static pa_status_t check_cache_args(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t kv_dtype, int64_t* row_bytes) {
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (!valid_dtype(kv_dtype)) return PA_ERR_DTYPE;
+  const int64_t rb = (int64_t)num_kv_heads * head_dim * dtype_bytes(kv_dtype);
+  if (rb % 16 != 0 || rb > ((int64_t)1 << 30)) return PA_ERR_UNSUPPORTED;
+  *row_bytes = rb;
+  return PA_OK;
+}
+
+pa_status_t pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t kv_dtype, void* stream) {
+  int64_t row_bytes = 0;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  pa_status_t st = check_cache_args(num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
+                                    &row_bytes);
+  if (st != PA_OK) return st;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_ALIGN;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (pa::launch_cache_write(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                             (int32_t)row_bytes, num_slots,
+                             static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
+pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
+                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                          void* stream) {
+  int64_t row_bytes = 0;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  pa_status_t st = check_cache_args(num_kv_heads, head_dim, block_size, num_blocks, kv_dtype,
+                                    &row_bytes);
+  if (st != PA_OK) return st;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_dst_pairs) return PA_ERR_NULL;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(src_dst_pairs, 8))
+    return PA_ERR_ALIGN;
+  if (pa::launch_block_copy(k_pool, v_pool, src_dst_pairs, num_pairs, row_bytes * block_size,
+                            num_blocks, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
+}  // extern "C"
