@@ -52,7 +52,10 @@ pa_status_t check_desc(const pa_decode_desc_t* d, int32_t max_context_len) {
     return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_context_len > (int64_t)d->max_blocks_per_seq * pa::kBlockTokens)
     return PA_ERR_SHAPE;
-  if (d->batch > 65535 || d->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;  // grid y/z
+  // sequences and partitions are the grid's y and z dimensions
+  if (d->batch > 65535) return PA_ERR_UNSUPPORTED;
+  const int32_t part = d->partition_size ? d->partition_size : pa::kDefaultPartitionTokens;
+  if ((max_context_len + part - 1) / part > 65535) return PA_ERR_UNSUPPORTED;
   // byte offsets inside one physical block must fit 32 bits; pool size must fit size_t
   const int64_t block_bytes =
       (int64_t)pa::kBlockTokens * d->num_kv_heads * d->head_dim * dtype_bytes(d->kv_dtype);

@@ -8,7 +8,7 @@
 // softmax exactly in real arithmetic.
 //
 // How it maps onto CDNA4
-//   * Work item = (partition of P blocks, kv head g, sequence b); one workgroup of 4
+//   * Work item = (kv head g, sequence b, partition of P blocks); one workgroup of 4
 //     waves per item. Wave w takes the partition's blocks w, w+4, w+8, ...; the G query
 //     heads sharing kv head g are all served by the same K/V bytes, read once.
 //   * QK^T runs on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}, fp8 converted to
@@ -87,6 +87,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), other counters untouched
   __builtin_amdgcn_wave_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Raw buffer loads: the block base lives in a scalar descriptor, each lane adds a
+// constant 32-bit offset. Offsets at or beyond `bytes` read as zero without touching
+// memory, which gives past-the-end prefetches for free (bytes = 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -197,8 +207,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
   constexpr int COMB_FLOATS = NW * G * (D + 2);
   __shared__ float smem[LOOP_FLOATS > COMB_FLOATS ? LOOP_FLOATS : COMB_FLOATS];
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // Grid (kv head, sequence, partition): workgroups are handed to the 8 XCDs round-robin
+  // in linear order, so the kv head varies fastest (for 8 kv heads each XCD serves one
+  // head and keeps its slices of shared blocks in its own L2) and the partition slowest
+  // (every sequence has partition 0; the empty tail partitions are dispatched last).
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // the wave index is uniform within a wave; say so, so that everything derived from it
+  // (block ranges, buffer descriptors) stays in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
 
   const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.max_context_len);
@@ -234,12 +251,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
   if (lane < nwb)
     my_id = a.block_tables[(size_t)b * a.max_blocks_per_seq + jbeg + wave + NW * lane];
 
-  const size_t tok_stride = (size_t)Hkv * ROWB;        // bytes between tokens of a block
-  const size_t blk_stride = kBlockTokens * tok_stride;  // bytes between physical blocks
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * ROWB;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * ROWB;
-  const uint32_t koff = (uint32_t)((lane & 15) * tok_stride + (lane >> 4) * 16);
-  const uint32_t voff = (uint32_t)((lane / LPR) * tok_stride + (lane % LPR) * 16);
+  const uint32_t tok_stride = (uint32_t)Hkv * ROWB;       // bytes between tokens of a block
+  const uint32_t blk_stride = kBlockTokens * tok_stride;  // bytes between physical blocks
+  const uint8_t* const kpool = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* const vpool = static_cast<const uint8_t*>(a.v_pool);
+  // per-lane byte offsets inside a block (constant over the loop)
+  const uint32_t koff = (uint32_t)g * ROWB + (lane & 15) * tok_stride + (lane >> 4) * 16;
+  const uint32_t voff = (uint32_t)g * ROWB + (lane / LPR) * tok_stride + (lane % LPR) * 16;
 
   float m[HPL], lsum[HPL];
 #pragma unroll
@@ -255,19 +273,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
 
   float* const pw = smem + wave * 2 * PBUF;  // this wave's two p/alpha buffers
 
-  auto block_id = [&](int k, bool& valid) -> int {
-    int pid = __builtin_amdgcn_readlane(my_id, k);
-    valid = (unsigned)pid < (unsigned)a.num_blocks;
-    return valid ? pid : 0;
-  };
-  auto load = [&](int pid, u32x4(&kb)[NL], u32x4(&vb)[NL]) {
-    const uint8_t* kp = kbase + (size_t)pid * blk_stride + koff;
-    const uint8_t* vp = vbase + (size_t)pid * blk_stride + voff;
+  // Issue the loads of the wave's k-th block. Always issues the same instructions so the
+  // compiler's wait counts stay static; k >= nwb (or a bad block id) loads from an
+  // empty descriptor and yields zeros without memory traffic.
+  auto issue = [&](int k, u32x4(&kb)[NL], u32x4(&vb)[NL], bool& valid) {
+    const bool real = k < nwb;
+    const int pid = __builtin_amdgcn_readlane(my_id, real ? k : 0);
+    valid = real && (unsigned)pid < (unsigned)a.num_blocks;
+    const size_t base = valid ? (size_t)pid * blk_stride : 0;
+    const uint32_t bytes = valid ? blk_stride : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, bytes);
 #pragma unroll
-    for (int s = 0; s < NL; ++s) kb[s] = *reinterpret_cast<const u32x4*>(kp + s * 64);
+    for (int s = 0; s < NL; ++s) kb[s] = buf_load16(rk, koff + s * 64);
 #pragma unroll
-    for (int i = 0; i < NL; ++i)
-      vb[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)i * RPI * tok_stride);
+    for (int i = 0; i < NL; ++i) vb[i] = buf_load16(rv, voff + i * RPI * tok_stride);
   };
   auto compute = [&](int j, bool valid, const u32x4(&kb)[NL], const u32x4(&vb)[NL],
                      float* P) {
@@ -339,18 +359,19 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- main loop over this wave's blocks, two register buffers in ping-pong
+  // ---- main loop over this wave's blocks: two register buffers, the next block's
+  // loads always in flight while the current block is computed
   if (nwb > 0) {
     u32x4 k0[NL], v0[NL], k1[NL], v1[NL];
     bool val0, val1;
-    load(block_id(0, val0), k0, v0);
+    issue(0, k0, v0, val0);
+    issue(1, k1, v1, val1);
     for (int k = 0; k < nwb; k += 2) {
       const int j0 = jbeg + wave + NW * k;
-      if (k + 1 < nwb) load(block_id(k + 1, val1), k1, v1);
       compute(j0, val0, k0, v0, pw);
-      if (k + 1 >= nwb) break;
-      if (k + 2 < nwb) load(block_id(k + 2, val0), k0, v0);
-      compute(j0 + NW, val1, k1, v1, pw + PBUF);
+      issue(k + 2, k0, v0, val0);
+      if (k + 1 < nwb) compute(j0 + NW, val1, k1, v1, pw + PBUF);
+      issue(k + 3, k1, v1, val1);
     }
   }
 
@@ -447,7 +468,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 template <int KV, int QT, int OT, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& args, int batch, hipStream_t stream) {
-  dim3 grid(args.max_parts, args.num_kv_heads, batch);
+  dim3 grid(args.num_kv_heads, batch, args.max_parts);
   decode_kernel<KV, QT, OT, D, G, kDecodeWaves><<<grid, kDecodeWaves * kWave, 0, stream>>>(args);
   return hipGetLastError();
 }
