@@ -103,6 +103,9 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, copy a buffer of this many MiB a few "
+                         "times (a reference kernel of known traffic for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -123,6 +126,16 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 3}), flush=True)
+        return 0
 
     log(f"building workload {args.config}")
     t0 = time.perf_counter()
