@@ -163,10 +163,10 @@ def main() -> int:
     out = torch.empty(tuple(w.q.shape), dtype=out_dtype, device="cuda")
     desc = pa.binding.make_desc(q, ks[0], tables, out, part)
     ws_bytes = pa.pa_decode_workspace_bytes(desc, w.max_context_len)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    resolved_part = pa.pa_decode_partition_size(desc, w.max_context_len)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    chunks = pa.pa_decode_max_chunks(desc, w.max_context_len)
     torch.cuda.synchronize()
-    log(f"resident: {R} pool replicas, workspace {ws_bytes} B, partition {resolved_part}")
+    log(f"resident: {R} pool replicas, workspace {ws_bytes} B, up to {chunks} work chunks")
 
     n_ev = args.steps
     dec0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -215,7 +215,7 @@ def main() -> int:
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "accumulate": "f32",
             "context_tokens": w.total_tokens, "max_context_len": w.max_context_len,
-            "kv_bytes_per_step": w.kv_bytes, "partition_size": resolved_part,
+            "kv_bytes_per_step": w.kv_bytes, "partition_size": part, "max_work_chunks": chunks,
             "pool_replicas": R, "seed": w.seed,
         },
         "tokens_per_s": w.batch / (ms * 1e-3),

@@ -53,7 +53,8 @@ typedef enum {
 } pa_status_t;
 
 /* Shape of one decode call.
- *   batch               B, sequences (one query token each); 0 is allowed (no-op)
+ *   batch               B, sequences (one query token each); 0 is allowed (no-op);
+ *                       at most 4096, and B * max_blocks_per_seq < 2^31
  *   num_q_heads         Hq
  *   num_kv_heads        Hkv; Hq % Hkv == 0; group G = Hq / Hkv in {1, 2, 4, 8}
  *   head_dim            d in {64, 128}
@@ -63,8 +64,15 @@ typedef enum {
  *   q_dtype, kv_dtype, out_dtype   pa_dtype_t codes; supported (q, kv, out):
  *                       (F32,F32,F32) (F16,F16,F16|F32) (BF16,BF16,BF16|F32)
  *                       (BF16,FP8_E4M3,BF16|F32)
- *   partition_size      tokens per split-KV partition; 0 = library default;
- *                       otherwise a multiple of 16 in [16, 4096] */
+ *   partition_size      0 (default): the KV work is cut into chunks balanced over the
+ *                       device: each workgroup starts with an equal static chunk (about
+ *                       70% of the work) and then takes small chunks as it finishes, so
+ *                       faster compute units do more. A sequence is cut only where a
+ *                       chunk ends. Otherwise a multiple of 16 (tokens): every chunk is
+ *                       that long (fixed-size split-KV partitions, all taken on demand),
+ *                       so no piece of a sequence is longer. A call whose chunks could
+ *                       exceed 16384 is rejected (UNSUPPORTED). The cut points depend on
+ *                       the lengths only, so results are bitwise reproducible. */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;
@@ -85,14 +93,16 @@ int32_t pa_abi_version(void);
 /* Human-readable text for a pa_status_t value; never NULL, static storage. */
 const char* pa_status_string(int32_t status);
 
-/* Partition size (tokens) pa_decode will use for this descriptor and max_context_len,
- * or a negative pa_status_t if the descriptor is invalid. */
-int32_t pa_decode_partition_size(const pa_decode_desc_t* desc, int32_t max_context_len);
+/* Most chunks (see partition_size) a call with this descriptor and max_context_len can
+ * have, or a negative pa_status_t if the descriptor is invalid. */
+int32_t pa_decode_max_chunks(const pa_decode_desc_t* desc, int32_t max_context_len);
 
-/* Bytes of device workspace pa_decode needs (0 when every sequence fits in one
- * partition). The workspace holds, for each (sequence, query head, partition), the
- * partition's running max m (log2 domain), normaliser l and unnormalised output
- * acc[d], all fp32. Returns 0 for an invalid descriptor. */
+/* Bytes of device workspace pa_decode needs (0 for an invalid descriptor or B = 0).
+ * The workspace holds two chunk counters, for each chunk the (m, l, acc) records of the
+ * at most two sequence pieces it leaves unfinished (running max m in log2 units,
+ * normaliser l and unnormalised output acc[d], fp32, per kv head and query head), and
+ * the per-sequence prefix sums of block counts. It must be zero-filled before its first
+ * use; every call leaves the counters at zero again, so later calls need no clearing. */
 size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_context_len);
 
 /* Decode attention over the paged KV cache.
@@ -104,10 +114,11 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_conte
  * computed blockwise: every 16-token block contributes its local max and normaliser,
  * merged by FlashAttention-style rescaling, which equals the global softmax
  * (vLLM-PagedAttention与连续批处理技术拆解, sections 3.1-3.3; block-table lookup as in
- * the paged_attention sketch of "AI vLLM：PagedAttention不够用了之后"). Sequences
- * longer than one partition are split; each partition's (m, l, acc) is merged by a
- * second kernel with the same rescaling. Positions >= L are never attended, whatever
- * the slots hold (NaN included). L == 0 gives a zero output.
+ * the paged_attention sketch of "AI vLLM：PagedAttention不够用了之后"). A sequence
+ * whose blocks span several work shares is split into pieces; each piece's (m, l, acc)
+ * is merged by a second kernel with the same rescaling. Positions >= L are never
+ * attended, whatever the slots hold (NaN included). L == 0 gives a zero output.
+ * Two kernels are enqueued: the decode and the merge.
  *
  * Arguments (device pointers unless noted):
  *   out            [B, Hq, d] out_dtype, written
@@ -118,8 +129,10 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_conte
  *   max_context_len host int >= every context_lens[b]; sizes the launch (no device sync)
  *   scale          host float, usually 1/sqrt(d)
  *   k_scale, v_scale host floats, dequantisation scales for fp8 pools (use 1 otherwise)
- *   workspace, workspace_bytes  device scratch of at least pa_decode_workspace_bytes();
- *                  may be NULL when that is 0; contents need no initialisation
+ *   workspace, workspace_bytes  device scratch of at least pa_decode_workspace_bytes()
+ *                  (always needed when B > 0), zero-filled before its first use (see
+ *                  pa_decode_workspace_bytes); calls that share a workspace must not
+ *                  overlap
  * All pointers must be 16-byte aligned. */
 pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
                       const void* k_pool, const void* v_pool,

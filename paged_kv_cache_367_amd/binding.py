@@ -48,8 +48,8 @@ def load_library():
     lib.pa_abi_version.argtypes = []
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [I32]
-    lib.pa_decode_partition_size.restype = I32
-    lib.pa_decode_partition_size.argtypes = [D, I32]
+    lib.pa_decode_max_chunks.restype = I32
+    lib.pa_decode_max_chunks.argtypes = [D, I32]
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_decode_workspace_bytes.argtypes = [D, I32]
     lib.pa_decode.restype = I32
@@ -113,8 +113,16 @@ def make_desc(q, k_pool, block_tables, out=None, partition_size: int = 0) -> Dec
                       partition_size)
 
 
-def pa_decode_partition_size(desc: DecodeDesc, max_context_len: int) -> int:
-    return load_library().pa_decode_partition_size(ctypes.byref(desc), max_context_len)
+def pa_decode_max_chunks(desc: DecodeDesc, max_context_len: int) -> int:
+    return load_library().pa_decode_max_chunks(ctypes.byref(desc), max_context_len)
+
+
+def decode_workspace(desc: DecodeDesc, max_context_len: int, device="cuda"):
+    """A zero-filled workspace tensor for pa_decode (zero before first use; pa_decode
+    leaves it ready for the next call)."""
+    import torch
+    n = load_library().pa_decode_workspace_bytes(ctypes.byref(desc), int(max_context_len))
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def pa_decode_workspace_bytes(desc: DecodeDesc, max_context_len: int) -> int:
@@ -124,8 +132,9 @@ def pa_decode_workspace_bytes(desc: DecodeDesc, max_context_len: int) -> int:
 def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
               scale: float, k_scale: float = 1.0, v_scale: float = 1.0, workspace=None,
               partition_size: int = 0, stream=None):
-    """Decode attention into `out` [B, Hq, d]. workspace: a uint8 GPU tensor of at least
-    pa_decode_workspace_bytes() bytes (allocated here when None and needed)."""
+    """Decode attention into `out` [B, Hq, d]. workspace: a zero-initialised uint8 GPU
+    tensor of at least pa_decode_workspace_bytes() bytes (allocated here, zero-filled,
+    when None)."""
     import torch
     lib = load_library()
     if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
@@ -137,7 +146,7 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_le
     desc = make_desc(q, k_pool, block_tables, out, partition_size)
     need = lib.pa_decode_workspace_bytes(ctypes.byref(desc), int(max_context_len))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.pa_decode(ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <limits.h>
 
 #include "../../include/paged_attention.h"
 #include "pa_launch.h"
@@ -33,6 +34,26 @@ bool supported_combo(int32_t q, int32_t kv, int32_t out) {
   return false;
 }
 
+// Workgroups of the decode: 8 waves per CU on the 256 CUs, NW waves each.
+int num_workgroups(const pa_decode_desc_t* d) {
+  return pa::kDeviceCUs * pa::kWavesPerCU / pa::group_waves(d->num_kv_heads);
+}
+
+// Units per chunk for an explicit partition size (0: default split).
+int part_units(const pa_decode_desc_t* d) { return d->partition_size / pa::kBlockTokens; }
+
+// Most chunks a call can have, which sizes the records in the workspace: the W static
+// ones, plus with fixed partitions every partition of the largest possible unit count.
+int64_t max_chunks(const pa_decode_desc_t* d, int32_t max_context_len) {
+  const int W = num_workgroups(d);
+  const int pu = part_units(d);
+  if (pu == 0) return W;
+  const int nw = pa::group_waves(d->num_kv_heads);
+  const int64_t seq_blocks = ((int64_t)max_context_len + pa::kBlockTokens - 1) / pa::kBlockTokens;
+  const int64_t units = (int64_t)(d->num_kv_heads / nw) * d->batch * seq_blocks;
+  return (int64_t)W + (units + pu - 1) / pu;
+}
+
 pa_status_t check_desc(const pa_decode_desc_t* d, int32_t max_context_len) {
   if (!d) return PA_ERR_NULL;
   if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
@@ -52,32 +73,41 @@ pa_status_t check_desc(const pa_decode_desc_t* d, int32_t max_context_len) {
     return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_context_len > (int64_t)d->max_blocks_per_seq * pa::kBlockTokens)
     return PA_ERR_SHAPE;
-  // sequences and partitions are the grid's y and z dimensions
-  if (d->batch > 65535) return PA_ERR_UNSUPPORTED;
-  const int32_t part = d->partition_size ? d->partition_size : pa::kDefaultPartitionTokens;
-  if ((max_context_len + part - 1) / part > 65535) return PA_ERR_UNSUPPORTED;
-  // byte offsets inside one physical block must fit 32 bits; pool size must fit size_t
+  // the batch's lengths and block prefix sums are kept in LDS
+  if (d->batch > pa::kMaxBatch) return PA_ERR_UNSUPPORTED;
+  // unit counts are 32-bit on the device; head groups and sequences are packed in 12 and
+  // 16 bits
+  const int64_t head_groups = d->num_kv_heads / pa::group_waves(d->num_kv_heads);
+  if (head_groups * d->batch * d->max_blocks_per_seq > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (head_groups >= 4096) return PA_ERR_UNSUPPORTED;
+  // byte offsets inside one physical block must fit 32 bits
   const int64_t block_bytes =
       (int64_t)pa::kBlockTokens * d->num_kv_heads * d->head_dim * dtype_bytes(d->kv_dtype);
   if (block_bytes > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
+  if (max_chunks(d, max_context_len) > pa::kMaxChunks) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
-int32_t resolve_partition(const pa_decode_desc_t* d) {
-  return d->partition_size ? d->partition_size : pa::kDefaultPartitionTokens;
-}
-
-int32_t max_parts_for(const pa_decode_desc_t* d, int32_t max_context_len) {
-  const int32_t part = resolve_partition(d);
-  const int32_t n = (max_context_len + part - 1) / part;
-  return n > 0 ? n : 1;
-}
-
-size_t ws_acc_bytes(const pa_decode_desc_t* d, int32_t max_parts) {
-  return (size_t)d->batch * d->num_q_heads * max_parts * d->head_dim * sizeof(float);
-}
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace: the two chunk counters (zero between calls), the records of cut segments,
+// then the per-sequence block prefix sums.
+struct Workspace {
+  size_t counters, acc, ml, prefix, total;   // byte offsets and size
+};
+Workspace workspace_layout(const pa_decode_desc_t* d, int32_t max_context_len) {
+  const size_t chunks = (size_t)max_chunks(d, max_context_len);
+  const size_t nw = (size_t)pa::group_waves(d->num_kv_heads);
+  const size_t group = (size_t)(d->num_q_heads / d->num_kv_heads);
+  const size_t recs = chunks * 2 * nw * group;       // (chunk, slot, wave, q head)
+  Workspace w;
+  w.counters = 0;
+  w.acc = 256;
+  w.ml = w.acc + align_up(recs * d->head_dim * sizeof(float), 256);
+  w.prefix = w.ml + align_up(recs * 2 * sizeof(float), 256);
+  w.total = w.prefix + align_up(((size_t)d->batch + 1) * sizeof(int32_t), 256);
+  return w;
+}
 
 }  // namespace
 
@@ -99,19 +129,16 @@ const char* pa_status_string(int32_t status) {
   }
 }
 
-int32_t pa_decode_partition_size(const pa_decode_desc_t* desc, int32_t max_context_len) {
+int32_t pa_decode_max_chunks(const pa_decode_desc_t* desc, int32_t max_context_len) {
   const pa_status_t st = check_desc(desc, max_context_len);
   if (st != PA_OK) return st;
-  return resolve_partition(desc);
+  return (int32_t)max_chunks(desc, max_context_len);
 }
 
 size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_context_len) {
-  if (check_desc(desc, max_context_len) != PA_OK) return 0;
-  const int32_t mp = max_parts_for(desc, max_context_len);
-  if (mp <= 1 || desc->batch == 0) return 0;
-  const size_t acc = align_up(ws_acc_bytes(desc, mp), 256);
-  const size_t ml = (size_t)desc->batch * desc->num_q_heads * mp * 2 * sizeof(float);
-  return acc + ml;
+  if (check_desc(desc, max_context_len) != PA_OK || desc->batch == 0) return 0;
+  const Workspace w = workspace_layout(desc, max_context_len);
+  return w.total;
 }
 
 pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
@@ -127,13 +154,12 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_ALIGN;
   if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_SHAPE;
-  const size_t need = pa_decode_workspace_bytes(desc, max_context_len);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
-  }
-  const int32_t part = resolve_partition(desc);
-  const int32_t mp = max_parts_for(desc, max_context_len);
+  const Workspace ws = workspace_layout(desc, max_context_len);
+  if (!workspace || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  char* wsb = static_cast<char*>(workspace);
+  const int nw = pa::group_waves(desc->num_kv_heads);
+  const int W = num_workgroups(desc);
 
   pa::DecodeArgs a;
   a.out = out;
@@ -142,40 +168,40 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            align_up(ws_acc_bytes(desc, mp), 256))
-                 : nullptr;
+  a.counters = reinterpret_cast<int32_t*>(wsb + ws.counters);
+  a.rec_acc = reinterpret_cast<float*>(wsb + ws.acc);
+  a.rec_ml = reinterpret_cast<float*>(wsb + ws.ml);
+  a.prefix = reinterpret_cast<int32_t*>(wsb + ws.prefix);
+  a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->num_kv_heads;
   a.num_blocks = desc->num_blocks;
   a.max_blocks_per_seq = desc->max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.part_blocks = part / pa::kBlockTokens;
-  a.max_parts = mp;
+  a.num_ranges = W;
+  a.part_units = part_units(desc);
   a.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = desc->num_q_heads / desc->num_kv_heads;
   if (pa::launch_decode(desc->q_dtype, desc->kv_dtype, desc->out_dtype, desc->head_dim, group, a,
-                        desc->batch, s) != hipSuccess)
+                        nw, s) != hipSuccess)
     return PA_ERR_HIP;
-  if (mp > 1) {
-    pa::MergeArgs m;
-    m.out = out;
-    m.context_lens = context_lens;
-    m.ws_acc = a.ws_acc;
-    m.ws_ml = a.ws_ml;
-    m.num_q_heads = desc->num_q_heads;
-    m.max_blocks_per_seq = desc->max_blocks_per_seq;
-    m.max_context_len = max_context_len;
-    m.part_blocks = a.part_blocks;
-    m.max_parts = mp;
-    m.v_scale = v_scale;
-    if (pa::launch_merge(desc->out_dtype, desc->head_dim, m, desc->batch, s) != hipSuccess)
-      return PA_ERR_HIP;
-  }
+  pa::MergeArgs m;
+  m.out = out;
+  m.rec_acc = a.rec_acc;
+  m.rec_ml = a.rec_ml;
+  m.prefix = a.prefix;
+  m.batch = desc->batch;
+  m.num_q_heads = desc->num_q_heads;
+  m.num_kv_heads = desc->num_kv_heads;
+  m.group_waves = nw;
+  m.num_ranges = W;
+  m.part_units = a.part_units;
+  m.v_scale = v_scale;
+  if (pa::launch_merge(desc->out_dtype, desc->head_dim, group, m, s) != hipSuccess)
+    return PA_ERR_HIP;
   return PA_OK;
 }
 

@@ -5,31 +5,40 @@
 // 16-token blocks found through the sequence's block table. Softmax is computed block
 // by block: each block contributes its local max and normaliser, and running results
 // are rescaled whenever the max moves (FlashAttention-style), which equals the global
-// softmax exactly in real arithmetic.
+// softmax exactly in real arithmetic. A long sequence is split into pieces whose
+// (max, normaliser, output) triples are merged the same way.
 //
 // How it maps onto CDNA4
-//   * Work item = (kv head g, sequence b, partition of P blocks); one workgroup of 4
-//     waves per item. Wave w takes the partition's blocks w, w+4, w+8, ...; the G query
-//     heads sharing kv head g are all served by the same K/V bytes, read once.
+//   * Persistent, balanced work split. A unit is one 16-token block of one sequence for
+//     one head group of NW kv heads (NW = 8 when Hkv allows). Units are numbered
+//     sequence by sequence; a fixed grid of W workgroups (8 waves per CU on the 256 CUs)
+//     takes equal contiguous shares, whatever the length mix. Wave w of a workgroup
+//     handles kv head hg*NW + w, so the NW waves read the NW head slices of the same
+//     blocks at the same time: each token row is read as one contiguous stretch.
+//   * Each wave streams its share as one pipeline over sequence boundaries: step s
+//     computes unit s while the K/V loads of the next NBUF units and the block-id loads
+//     of the NBUF after those are in flight. K/V loads are raw buffer loads from a
+//     per-block scalar descriptor; a unit past the share gets an empty descriptor, so
+//     the instruction stream (and every wait count) is the same at every step.
 //   * QK^T runs on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}, fp8 converted to
 //     bf16 first, v_mfma_f32_16x16x4f32 for fp32). Operand B is the K block exactly as
 //     it sits in HBM: lane (t, q) = (lane % 16, lane / 16) loads 16-byte chunk 4s+q of
-//     token t's row, so each load instruction covers 64 contiguous bytes of 16 rows and
-//     no shuffle or LDS pass is needed. Operand A repeats the G query rows over the 16
-//     MFMA rows (row i holds head i % G), so after the MFMA every lane holds the scores
-//     of its token for G distinct heads.
+//     token t's row. Operand A repeats the G query rows over the 16 MFMA rows (row i
+//     holds head i % G), so after the MFMA every lane holds its token's scores for the
+//     G heads. The q rows arrive with the first block of a piece and are laid out for
+//     the MFMA through LDS.
 //   * Block max: 16-lane DPP row reduction. Probabilities p[t][h] go to LDS once per
 //     block and are read back broadcast by the V stage.
-//   * PV on the vector ALU in fp32: lane (r, c) owns 16-byte chunk c of V rows r,
-//     r + RPI, ... and accumulates acc[h][e] for all G heads, so every V byte is
-//     converted once and used G times. At the end, lanes owning the same chunk are
-//     summed (xor shuffles), then the 4 waves are merged through LDS.
-//   * One partition covers the whole sequence: the final output is written directly.
-//     Otherwise (m, l, acc) go to the workspace and merge_kernel combines them.
+//   * PV on the vector ALU in fp32: lane (r, c) owns a V chunk c of rows r, r + RPI, ...
+//     and accumulates acc[h][e] for all G heads, so every V byte is converted once and
+//     used G times. At the end of a piece, lanes owning the same chunk are summed.
+//   * A sequence whose segment lies in one share is written out directly. A segment cut
+//     by share boundaries leaves one (m, l, acc) record per piece (at most two per wave:
+//     the share's first and last segment), and merge_kernel combines them.
 //   * The partial last block is masked by selection (scores -> -inf, V -> 0), so stale
 //     or NaN slots past L never reach the result.
-//   * Reduction order depends on logical positions only, never on physical block ids,
-//     so moving blocks in the pool leaves the output bitwise unchanged.
+//   * Reduction order depends on logical positions and lengths only, never on physical
+//     block ids, so moving blocks in the pool leaves the output bitwise unchanged.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,10 +50,15 @@ namespace pa {
 namespace {
 
 constexpr int kWave = 64;
+#ifndef PA_RING_BYTES
+#define PA_RING_BYTES 16384
+#endif
+constexpr int kRingBytes = PA_RING_BYTES;  // K and V bytes in flight per wave (ring depth)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -98,6 +112,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
+}
+template <int BYTES> struct VChunk;
+template <> struct VChunk<16> {
+  using type = u32x4;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return buf_load16(r, o);
+  }
+};
+template <> struct VChunk<8> {
+  using type = u32x2;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return buf_load8(r, o);
+  }
+};
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
@@ -149,7 +179,18 @@ __device__ __forceinline__ f32x4 qk_chunk(f32x4 acc, u32x4 k, const u32x4* qc) {
   return acc;
 }
 
-// One 16-byte V chunk -> fp32 values.
+// One V chunk (8 bytes of fp8, else 16 bytes) -> fp32 values.
+__device__ __forceinline__ void v_chunk_fp8(u32x2 w, float* v) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    v[4 * i] = lo[0];
+    v[4 * i + 1] = lo[1];
+    v[4 * i + 2] = hi[0];
+    v[4 * i + 3] = hi[1];
+  }
+}
 template <int KV>
 __device__ __forceinline__ void v_chunk(u32x4 w, float* v) {
   if constexpr (KV == PA_BF16) {
@@ -164,139 +205,328 @@ __device__ __forceinline__ void v_chunk(u32x4 w, float* v) {
     const f16x8 h = __builtin_bit_cast(f16x8, w);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
-  } else if constexpr (KV == PA_FP8_E4M3) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-      f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-      v[4 * i] = lo[0];
-      v[4 * i + 1] = lo[1];
-      v[4 * i + 2] = hi[0];
-      v[4 * i + 3] = hi[1];
-    }
   } else {
+    static_assert(KV == PA_F32, "fp8 V chunks are 8 bytes (v_chunk_fp8)");
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
   }
 }
 
-__device__ __forceinline__ int clamp_len(int L, int max_blocks_per_seq, int max_context_len) {
+// Context length clamped to [0, cap]; cap = min(table width * 16, max_context_len).
+__device__ __forceinline__ int clamp_len(int L, int cap) {
   L = L < 0 ? 0 : L;
-  int cap = max_blocks_per_seq * kBlockTokens;
-  cap = cap < max_context_len ? cap : max_context_len;
   return L < cap ? L : cap;
 }
+__device__ __forceinline__ int nblocks(int L) { return (L + kBlockTokens - 1) / kBlockTokens; }
 
-template <int KV, int QT, int OT, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
+// Full-wave reductions (xor butterfly over all 64 lanes).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int st = 1; st < kWave; st <<= 1) x = fmaxf(x, __shfl_xor(x, st));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+
+// Register allocation target: 8 waves per CU (2 per SIMD), i.e. at most 256 VGPRs.
+constexpr int kMaxThreads = kMaxGroupWaves * kWave;
+
+// Per-unit bookkeeping carried (in scalar registers) from the id fetch to the K/V issue
+// to the compute stage.
+// Unit flags: valid; first / last unit of a piece (the part of a segment inside one
+// chunk); the piece starts its chunk; the unit is the first / last block of its segment.
+enum : int { kValid = 1, kFirst = 2, kLast = 4, kAtStart = 8, kSegStart = 16, kSegEnd = 32 };
+// Packed so that the ring's bookkeeping stays in a few scalar registers:
+//   bf = b | flags << 16 | rem << 24   (rem: tokens of the block below L, 1..16)
+//   hc = head group | chunk << 12
+struct UnitMeta {
+  int bf, j, hc;
+  __device__ int b() const { return bf & 0xffff; }
+  __device__ int flags() const { return (bf >> 16) & 0xff; }
+  __device__ int rem() const { return bf >> 24; }
+  __device__ int hg() const { return hc & 0xfff; }
+  __device__ int chunk() const { return hc >> 12; }
+};
+
+template <int KV, int QT, int OT, int D, int G>
+__global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   constexpr int KB = Enc<KV>::bytes;
   constexpr int QB = Enc<QT>::bytes;
   constexpr int ROWB = D * KB;            // bytes of one token's K (or V) row, one kv head
-  constexpr int NL = ROWB / 64;           // 16-byte loads per lane per block, K and V each
-  constexpr int EPC = 16 / KB;            // elements per 16-byte chunk
-  constexpr int LPR = ROWB / 16;          // V stage: lanes per token row
-  constexpr int RPI = kWave / LPR;        // V stage: token rows per load instruction
+  constexpr int NL = ROWB / 64;           // K: 16-byte loads per lane per block
+  constexpr int EPC = 16 / KB;            // K: elements per 16-byte chunk
+  // V stage: each lane loads VB-byte pieces (8 for fp8, so that a lane's accumulators
+  // stay at 8 elements per head), LPR lanes per token row, RPI rows per instruction
+  constexpr int VB = KB == 1 ? 8 : 16;
+  constexpr int VEPC = VB / KB;
+  constexpr int LPR = ROWB / VB;
+  constexpr int RPI = kWave / LPR;
+  constexpr int NLV = kBlockTokens / RPI; // V: loads per lane per block
+  using VT = typename VChunk<VB>::type;
   constexpr int QROWS = G > 4 ? G / 4 : 1;  // MFMA row groups holding distinct heads
   constexpr int HPL = G < 4 ? G : 4;        // distinct heads per lane after the MFMA
   constexpr int QCH = EPC * QB / 16;        // 16-byte q pieces matching one K chunk
-  static_assert(NL >= 1 && NL * RPI == kBlockTokens, "block layout");
+  constexpr int QBYTES = G * D * QB;        // the G query rows of one (sequence, kv head)
+  constexpr int QPL = (QBYTES + kWave * 16 - 1) / (kWave * 16);  // q pieces per lane
+  static_assert(NL >= 1 && LPR <= kWave && NLV * RPI == kBlockTokens, "block layout");
   static_assert(QCH >= 1, "q layout");
-
+  // ring depth NBUF (units in flight while one more is computed): about kRingBytes of
+  // K and V per wave, at most 3, and few enough that the R = NBUF + 1 register slots fit
+  // the 256 registers of 2 waves per SIMD next to the accumulators and q operand
+  constexpr int BLK_WAVE_BYTES = (NL * 16 + NLV * VB) * kWave;  // K + V of one block, one wave
+  constexpr int SLOT_VGPRS = NL * 4 + NLV * (VB / 4) + QPL * 4 + 1;
+  constexpr int FIXED_VGPRS = G * VEPC + NL * QCH * 4 + 2 * G + 80;
+  constexpr int NBUF_FIT = (256 - FIXED_VGPRS) / SLOT_VGPRS - 1;
+  constexpr int NBUF_BYTES = kRingBytes / BLK_WAVE_BYTES;
+  constexpr int NBUF_MIN = NBUF_BYTES < NBUF_FIT ? NBUF_BYTES : NBUF_FIT;
+  constexpr int NBUF = NBUF_MIN < 1 ? 1 : (NBUF_MIN > 3 ? 3 : NBUF_MIN);
   constexpr int PBUF = kBlockTokens * G + 8;    // p[16][G] + alpha[8], one block, one wave
-  constexpr int LOOP_FLOATS = NW * 2 * PBUF;
-  constexpr int COMB_FLOATS = NW * G * (D + 2);
-  __shared__ float smem[LOOP_FLOATS > COMB_FLOATS ? LOOP_FLOATS : COMB_FLOATS];
 
-  // Grid (kv head, sequence, partition): workgroups are handed to the 8 XCDs round-robin
-  // in linear order, so the kv head varies fastest (for 8 kv heads each XCD serves one
-  // head and keeps its slices of shared blocks in its own L2) and the partition slowest
-  // (every sequence has partition 0; the empty tail partitions are dispatched last).
-  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  __shared__ int s_lens[kMaxBatch];        // clamped context length per sequence
+  __shared__ int s_pre[kMaxBatch + 1];     // blocks before each sequence
+  __shared__ int s_wsum[kMaxGroupWaves];
+  __shared__ int s_next[2];                // next chunk of the workgroup, by parity
+  __shared__ float s_p[kMaxGroupWaves][2 * PBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[kMaxGroupWaves][QBYTES];
+
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  // the wave index is uniform within a wave; say so, so that everything derived from it
-  // (block ranges, buffer descriptors) stays in scalar registers
+  const int nthr = blockDim.x;
+  const int NW = nthr / kWave;
+  // uniform within a wave; say so, so that everything derived stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int B = a.batch, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int HGC = Hkv / NW;                          // head groups
+  const int cap = min(a.max_blocks_per_seq * kBlockTokens, a.max_context_len);
 
-  const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.max_context_len);
-  const int nb = (L + kBlockTokens - 1) / kBlockTokens;
-  const int nparts = (nb + a.part_blocks - 1) / a.part_blocks;
-  if (L == 0) {  // nothing to attend: zero output
-    if (part == 0)
-      for (int idx = tid; idx < G * D; idx += NW * kWave)
-        store_out<OT>(a.out, ((size_t)b * Hq + g * G) * D + idx, 0.0f);
-    return;
+  // ---- 1. lengths and block prefix sums of the whole batch, in LDS. Thread t owns the
+  // sequences [t*K, t*K + K). Every workgroup computes them; workgroup 0 also stores the
+  // prefix sums for the merge.
+  const int K = (B + nthr - 1) / nthr;
+  const int b_lo = min(B, tid * K), b_hi = min(B, b_lo + K);
+  int mine = 0;
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int L = clamp_len(a.context_lens[b], cap);
+    s_lens[b] = L;
+    mine += nblocks(L);
   }
-  if (part >= nparts) return;
-  const int jbeg = part * a.part_blocks;
-  const int jend = min(nb, jbeg + a.part_blocks);
-
-  // ---- query operand: MFMA row i = lane % 16 carries head i % G; chunk c = 4s + lane/16
-  u32x4 qreg[NL][QCH];
+  int incl = mine;
+#pragma unroll
+  for (int st = 1; st < kWave; st <<= 1) {
+    const int y = __shfl_up(incl, st);
+    if (lane >= st) incl += y;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < NW; ++w) {
+    const int x = s_wsum[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
   {
-    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
-                          ((size_t)b * Hq + (size_t)g * G + (lane & 15) % G) * D * QB;
-#pragma unroll
-    for (int s = 0; s < NL; ++s) {
-      const int c = 4 * s + (lane >> 4);
-#pragma unroll
-      for (int u = 0; u < QCH; ++u)
-        qreg[s][u] = *reinterpret_cast<const u32x4*>(qrow + c * EPC * QB + u * 16);
+    int c = before + incl - mine;                    // blocks of sequences before b_lo
+    for (int b = b_lo; b < b_hi; ++b) {
+      s_pre[b] = c;
+      if (blockIdx.x == 0) a.prefix[b] = c;
+      c += nblocks(s_lens[b]);
+    }
+    if (tid == 0) {
+      s_pre[B] = total;
+      if (blockIdx.x == 0) a.prefix[B] = total;
     }
   }
 
-  // ---- this wave's physical block ids, one per lane, read back with readlane
-  const int nwb = jend - jbeg - wave > 0 ? (jend - jbeg - wave + NW - 1) / NW : 0;
-  int my_id = 0;
-  if (lane < nwb)
-    my_id = a.block_tables[(size_t)b * a.max_blocks_per_seq + jbeg + wave + NW * lane];
+  // ---- 2. chunks. T units. By default workgroup r takes static chunk r, dealt to the 8
+  // XCDs in contiguous eighths (workgroups go to XCDs round-robin) so that neighbouring
+  // sequences share an L2. With fixed partitions every chunk is taken from a counter.
+  const int W = a.num_ranges, bid = blockIdx.x;
+  const ChunkGeom cg = chunk_geometry((int64_t)HGC * total, W, a.part_units);
+  const int rng = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
+  int* const grab_ctr = a.counters;          // small chunks taken
+  int* const done_ctr = a.counters + 1;      // workgroups that found none left
+  uint32_t grab_v = 0;                       // wave 0, lane 0: pending counter value
+  uint32_t done_v = 0;
+  bool done_issued = false;
+  int tpar = 0;                              // parity of the chunk transition
+  __syncthreads();
+
+  // ---- 3. the unit walker (scalar): position in the current chunk, sequence, head
+  // group, block
+  int cur = -1;                              // current chunk, -1 once there is none
+  int wu = 0, cbeg = 0, cend = 0;
+  int wb = 0, whg = 0, wj = 0, wnb = 1, wL = 0;
+  auto locate = [&](int u) {                 // largest b with HGC * pre[b] <= u
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (HGC * s_pre[mid] <= u) lo = mid;
+      else hi = mid - 1;
+    }
+    wb = lo;
+    wL = s_lens[lo];
+    wnb = nblocks(wL);
+    const int rel = u - HGC * s_pre[lo];
+    whg = rel / wnb;
+    wj = rel - whg * wnb;
+  };
+  // Ask for the chunk after the current one. atomicInc (increment with a wrap bound that
+  // is never reached) rather than atomicAdd: the compiler turns a uniform atomicAdd into a
+  // wave-wide atomic whose result it waits for at once, which would drain the load ring.
+  auto grab = [&]() {
+    if (wave == 0 && lane == 0) grab_v = atomicInc(reinterpret_cast<unsigned*>(grab_ctr), ~0u);
+  };
+  auto enter = [&](int c) {
+    cur = c;
+    if (c < 0) return;
+    cbeg = (int)chunk_begin(cg, c);
+    cend = (int)chunk_end(cg, c);
+    wu = cbeg;
+    locate(wu);
+    grab();
+  };
+  // at a chunk end: wave 0 publishes the chunk it was given, all waves take it
+  auto next_chunk = [&]() {
+    if (wave == 0 && lane == 0) {
+      const bool none = grab_v >= (uint32_t)cg.nsmall;
+      s_next[tpar] = none ? -1 : W + (int)grab_v;
+      if (none && !done_issued) {
+        done_v = atomicInc(reinterpret_cast<unsigned*>(done_ctr), ~0u);
+        done_issued = true;
+      }
+    }
+    __syncthreads();
+    const int c = __builtin_amdgcn_readfirstlane(s_next[tpar]);
+    tpar ^= 1;
+    enter(c);
+  };
+  if (!cg.fixed && chunk_begin(cg, rng) < chunk_end(cg, rng)) {
+    enter(rng);
+  } else {
+    grab();
+    next_chunk();
+  }
+  auto snapshot = [&]() -> UnitMeta {
+    UnitMeta m;
+    int f = 0;
+    if (cur >= 0) {
+      f = kValid;
+      if (wj == 0) f |= kSegStart | kFirst;
+      if (wj == wnb - 1) f |= kSegEnd | kLast;
+      if (wu == cbeg) f |= kAtStart | kFirst;
+      if (wu == cend - 1) f |= kLast;
+    }
+    const int rem = min(kBlockTokens, wL - wj * kBlockTokens);
+    m.bf = wb | f << 16 | (rem > 0 ? rem : 0) << 24;
+    m.j = wj;
+    m.hc = whg | (cur >= 0 ? cur : 0) << 12;
+    return m;
+  };
+  auto advance = [&]() {
+    if (cur < 0) return;
+    if (++wu == cend) {
+      next_chunk();
+      return;
+    }
+    if (++wj < wnb) return;
+    wj = 0;
+    if (++whg < HGC) return;
+    whg = 0;
+    do {                  // wu < cend guarantees a non-empty sequence follows
+      ++wb;
+      wL = s_lens[wb];
+      wnb = nblocks(wL);
+    } while (wnb == 0 && wb + 1 < B);
+  };
 
   const uint32_t tok_stride = (uint32_t)Hkv * ROWB;       // bytes between tokens of a block
   const uint32_t blk_stride = kBlockTokens * tok_stride;  // bytes between physical blocks
   const uint8_t* const kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* const vpool = static_cast<const uint8_t*>(a.v_pool);
-  // per-lane byte offsets inside a block (constant over the loop)
-  const uint32_t koff = (uint32_t)g * ROWB + (lane & 15) * tok_stride + (lane >> 4) * 16;
-  const uint32_t voff = (uint32_t)g * ROWB + (lane / LPR) * tok_stride + (lane % LPR) * 16;
+  const uint8_t* const qbase = static_cast<const uint8_t*>(a.q);
+  // per-lane byte offsets inside one kv head's slice of a block (constant)
+  const uint32_t koff = (lane & 15) * tok_stride + (lane >> 4) * 16;
+  const uint32_t voff = (lane / LPR) * tok_stride + (lane % LPR) * VB;
 
-  float m[HPL], lsum[HPL];
-#pragma unroll
-  for (int r = 0; r < HPL; ++r) {
-    m[r] = neg_inf();
-    lsum[r] = 0.0f;
-  }
-  float acc[G][EPC];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
-
-  float* const pw = smem + wave * 2 * PBUF;  // this wave's two p/alpha buffers
-
-  // Issue the loads of the wave's k-th block. Always issues the same instructions so the
-  // compiler's wait counts stay static; k >= nwb (or a bad block id) loads from an
-  // empty descriptor and yields zeros without memory traffic.
-  auto issue = [&](int k, u32x4(&kb)[NL], u32x4(&vb)[NL], bool& valid) {
-    const bool real = k < nwb;
-    const int pid = __builtin_amdgcn_readlane(my_id, real ? k : 0);
-    valid = real && (unsigned)pid < (unsigned)a.num_blocks;
-    const size_t base = valid ? (size_t)pid * blk_stride : 0;
-    const uint32_t bytes = valid ? blk_stride : 0u;
+  // physical id of a unit's block (every lane reads the same word); zero-size descriptor
+  // for units past the range, so the load costs nothing
+  auto load_id = [&](const UnitMeta& m) -> uint32_t {
+    const bool v = m.flags() & kValid;
+    const int32_t* row = a.block_tables + (size_t)(v ? m.b() : 0) * a.max_blocks_per_seq;
+    return buf_load4(make_rsrc(row, v ? (uint32_t)a.max_blocks_per_seq * 4u : 0u),
+                     (uint32_t)m.j * 4u);
+  };
+  // K, V of the unit's block for this wave's kv head, and the head's q rows when the
+  // unit opens a piece. Always the same instructions, so wait counts stay static.
+  auto issue = [&](const UnitMeta& m, uint32_t idv, u32x4(&kb)[NL], VT(&vb)[NLV],
+                   u32x4(&qs)[QPL]) {
+    const int pid = __builtin_amdgcn_readfirstlane((int)idv);
+    const bool valid = (m.flags() & kValid) && (unsigned)pid < (unsigned)a.num_blocks;
+    const int g = m.hg() * NW + wave;
+    const size_t base = valid ? (size_t)pid * blk_stride + (size_t)g * ROWB : 0;
+    const uint32_t bytes = valid ? blk_stride - (uint32_t)g * ROWB : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, bytes);
+    const bool wantq = (m.flags() & (kValid | kFirst)) == (kValid | kFirst);
+    const size_t qo = wantq ? ((size_t)m.b() * Hq + (size_t)g * G) * D * QB : 0;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + qo, wantq ? (uint32_t)QBYTES : 0u);
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) qs[i] = buf_load16(rq, (uint32_t)(lane + kWave * i) * 16u);
 #pragma unroll
     for (int s = 0; s < NL; ++s) kb[s] = buf_load16(rk, koff + s * 64);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vb[i] = buf_load16(rv, voff + i * RPI * tok_stride);
+    for (int i = 0; i < NLV; ++i) vb[i] = VChunk<VB>::load(rv, voff + i * RPI * tok_stride);
   };
-  auto compute = [&](int j, bool valid, const u32x4(&kb)[NL], const u32x4(&vb)[NL],
-                     float* P) {
+
+  // ---- 4. running state of the current piece
+  u32x4 qreg[NL][QCH];
+  float m[HPL], lsum[HPL];
+  float acc[G][VEPC];
+  bool piece_whole_start = false;          // the current piece began at its segment's start
+  int piece_slot = 0;
+  float* const pw = &s_p[wave][0];
+  uint8_t* const qw = &s_q[wave][0];
+
+  auto compute = [&](const UnitMeta& mu, const u32x4(&kb)[NL], const VT(&vb)[NLV],
+                     const u32x4(&qs)[QPL], float* P) {
+    const int fl = mu.flags();
+    if (!(fl & kValid)) return;
+    const int g = mu.hg() * NW + wave;
+    if (fl & kFirst) {
+      // a new piece: fresh (m, l, acc), and this head's q rows into the MFMA A layout
+#pragma unroll
+      for (int r = 0; r < HPL; ++r) {
+        m[r] = neg_inf();
+        lsum[r] = 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEPC; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < QPL; ++i)
+        if ((lane + kWave * i) * 16 < QBYTES)
+          *reinterpret_cast<u32x4*>(qw + (lane + kWave * i) * 16) = qs[i];
+      wave_lds_sync();
+      const uint8_t* qrow = qw + ((lane & 15) % G) * D * QB;
+#pragma unroll
+      for (int s = 0; s < NL; ++s) {
+        const int c = 4 * s + (lane >> 4);
+#pragma unroll
+        for (int u = 0; u < QCH; ++u)
+          qreg[s][u] = *reinterpret_cast<const u32x4*>(qrow + c * EPC * QB + u * 16);
+      }
+      piece_whole_start = (fl & kSegStart) != 0;
+      piece_slot = (fl & kAtStart) ? 0 : 1;
+    }
+    const int rem = mu.rem();              // tokens of this block below L
+    const bool ragged = rem < kBlockTokens;
     // scores of token t = lane % 16 for the heads of MFMA rows 4*(lane/16) + r
     f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NL; ++s) sc = qk_chunk<KV>(sc, kb[s], qreg[s]);
-    const bool ragged = !valid || (j + 1) * kBlockTokens > L;
-    const bool tok_ok = valid && (j * kBlockTokens + (lane & 15) < L);
+    const bool tok_ok = (lane & 15) < rem;
     float al[HPL], p[HPL];
 #pragma unroll
     for (int r = 0; r < HPL; ++r) {
@@ -337,206 +567,305 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha[h];
+        for (int e = 0; e < VEPC; ++e) acc[h][e] *= alpha[h];
     }
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    for (int i = 0; i < NLV; ++i) {
       const int row = lane / LPR + RPI * i;
       float pv[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) pv[h] = P[row * G + h];
-      float v[EPC];
-      v_chunk<KV>(vb[i], v);
+      float v[VEPC];
+      if constexpr (KV == PA_FP8_E4M3) v_chunk_fp8(vb[i], v);
+      else v_chunk<KV>(vb[i], v);
       if (ragged) {
-        const bool ok = valid && (j * kBlockTokens + row < L);
+        const bool ok = row < rem;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) v[e] = ok ? v[e] : 0.0f;
+        for (int e = 0; e < VEPC; ++e) v[e] = ok ? v[e] : 0.0f;
       }
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
+        for (int e = 0; e < VEPC; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
+    }
+
+    if (!(fl & kLast)) return;
+    // ---- the piece ends here: reduce over lanes, then write the output (whole segment)
+    // or a record (a piece of a segment cut by a range boundary)
+#pragma unroll
+    for (int r = 0; r < HPL; ++r) lsum[r] = row16_sum(lsum[r]);
+#pragma unroll
+    for (int st = LPR; st < kWave; st <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEPC; ++e) acc[h][e] += __shfl_xor(acc[h][e], st);
+    float mh[G], lh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if constexpr (G > 4) {
+        mh[h] = __shfl(m[h & 3], (h >> 2) * 16);
+        lh[h] = __shfl(lsum[h & 3], (h >> 2) * 16);
+      } else {
+        mh[h] = m[h];
+        lh[h] = lsum[h];
+      }
+    }
+    if (piece_whole_start && (fl & kSegEnd)) {
+      if (lane < LPR) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const size_t o = ((size_t)mu.b() * Hq + (size_t)g * G + h) * D + VEPC * lane;
+          const float inv = lh[h] > 0.0f ? a.v_scale / lh[h] : 0.0f;
+#pragma unroll
+          for (int e = 0; e < VEPC; ++e) store_out<OT>(a.out, o + e, acc[h][e] * inv);
+        }
+      }
+    } else {
+      const size_t rec = ((size_t)mu.chunk() * 2 + piece_slot) * NW + wave;
+      if (lane < LPR) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < VEPC; ++e)
+            a.rec_acc[(rec * G + h) * D + VEPC * lane + e] = acc[h][e];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (lane == h) {
+          a.rec_ml[(rec * G + h) * 2] = mh[h];
+          a.rec_ml[(rec * G + h) * 2 + 1] = lh[h];
+        }
+      }
     }
   };
 
-  // ---- main loop over this wave's blocks: two register buffers, the next block's
-  // loads always in flight while the current block is computed
-  if (nwb > 0) {
-    u32x4 k0[NL], v0[NL], k1[NL], v1[NL];
-    bool val0, val1;
-    issue(0, k0, v0, val0);
-    issue(1, k1, v1, val1);
-    for (int k = 0; k < nwb; k += 2) {
-      const int j0 = jbeg + wave + NW * k;
-      compute(j0, val0, k0, v0, pw);
-      issue(k + 2, k0, v0, val0);
-      if (k + 1 < nwb) compute(j0 + NW, val1, k1, v1, pw + PBUF);
-      issue(k + 3, k1, v1, val1);
-    }
+  // ---- 5. the stream, over a ring of R = NBUF + 1 register slots (unit x lives in slot
+  // x % R). Step k first issues the K/V loads of unit k + NBUF into the slot unit k - 1
+  // has just left (its block id was loaded R steps earlier) and the id load of unit
+  // k + NBUF + R, then computes unit k: NBUF units stay in flight while one is computed.
+  // The ring is unrolled so that every slot index is a constant.
+  constexpr int R = NBUF + 1;
+  u32x4 kb[R][NL];
+  VT vb[R][NLV];
+  u32x4 qs[R][QPL];
+  uint32_t idv[R];
+  UnitMeta mk[R], mi[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    mi[u] = snapshot();
+    idv[u] = load_id(mi[u]);
+    advance();
   }
-
-  // ---- combine: lanes of a row (lsum), lanes sharing a V chunk (acc), then waves
 #pragma unroll
-  for (int r = 0; r < HPL; ++r) lsum[r] = row16_sum(lsum[r]);
-#pragma unroll
-  for (int st = LPR; st < kWave; st <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[h][e] += __shfl_xor(acc[h][e], st);
-
-  __syncthreads();  // every wave is done with its loop buffers
-  float* Wm = smem;
-  float* Wl = smem + NW * G;
-  float* Wa = smem + 2 * NW * G;
-  if ((lane & 15) == 0 && (lane >> 4) < QROWS) {
-    const int hb = G > 4 ? 4 * (lane >> 4) : 0;
-#pragma unroll
-    for (int r = 0; r < HPL; ++r) {
-      Wm[wave * G + hb + r] = m[r];
-      Wl[wave * G + hb + r] = lsum[r];
-    }
+  for (int u = 0; u < NBUF; ++u) {
+    mk[u] = mi[u];
+    issue(mk[u], idv[u], kb[u], vb[u], qs[u]);
+    mi[u] = snapshot();
+    idv[u] = load_id(mi[u]);
+    advance();
   }
-  if (lane < LPR) {
+  // every wave sees the same chunks, so the loop ends at the same step in all of them
+  for (;;) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int u = 0; u < R; ++u) {
+      const int si = (u + NBUF) % R;   // slot of unit k + NBUF (= slot of unit k - 1)
+      mk[si] = mi[si];
+      issue(mk[si], idv[si], kb[si], vb[si], qs[si]);
+      mi[si] = snapshot();
+      idv[si] = load_id(mi[si]);
+      advance();
+      compute(mk[u], kb[u], vb[u], qs[u], pw + (u & 1) * PBUF);
+    }
+    bool busy = cur >= 0;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) Wa[(wave * G + h) * D + EPC * lane + e] = acc[h][e];
+    for (int u = 0; u < R; ++u) busy |= ((mk[u].flags() | mi[u].flags()) & kValid) != 0;
+    if (!busy) break;
   }
-  __syncthreads();
-
-  for (int idx = tid; idx < G * D; idx += NW * kWave) {
-    const int h = idx / D, dd = idx % D;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, Wm[w * G + h]);
-    float Ls = 0.0f, A = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = Wm[w * G + h];
-      const float f = mw == neg_inf() ? 0.0f : fast_exp2(mw - M);
-      Ls = fmaf(Wl[w * G + h], f, Ls);
-      A = fmaf(Wa[(w * G + h) * D + dd], f, A);
-    }
-    const size_t hq = (size_t)b * Hq + (size_t)g * G + h;
-    if (nparts == 1) {
-      store_out<OT>(a.out, hq * D + dd, Ls > 0.0f ? a.v_scale * (A / Ls) : 0.0f);
-    } else {
-      const size_t slot = hq * a.max_parts + part;
-      a.ws_acc[slot * D + dd] = A;
-      if (dd == 0) {
-        a.ws_ml[slot * 2] = M;
-        a.ws_ml[slot * 2 + 1] = Ls;
-      }
-    }
+  // the last workgroup to run out of chunks resets the counters for the next call
+  if (wave == 0 && lane == 0 && done_issued && done_v == (uint32_t)(W - 1)) {
+    atomicExch(grab_ctr, 0);
+    atomicExch(done_ctr, 0);
   }
 }
 
-// Cross-partition merge with the same rescaling: M = max_p m_p,
-// out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-template <int OT, int D>
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int st = 1; st < kWave; st <<= 1) x += __shfl_xor(x, st);
+  return x;
+}
+
+// Combine the pieces of segments cut by chunk boundaries, with the same rescaling:
+// M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
+// waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
+// query head h. Wave w folds pieces w, w + MW, ... into a running (M, L, A) with the
+// online rule, UNROLL pieces per memory round trip (each piece's (m, l) and partial
+// output are loaded together); the MW partial results are then combined through LDS.
+template <int OT, int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int EPL = G * D / kWave;
+  constexpr int MW = 4, UNROLL = 4;
+  static_assert(EPL >= 1 && D % EPL == 0, "merge layout");
+  __shared__ float s_ml[MW][G][2];
+  __shared__ float s_acc[MW][G * D];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int hq = blockIdx.x * 4 + wave, b = blockIdx.y;
-  if (hq >= a.num_q_heads) return;
-  const int L = clamp_len(a.context_lens[b], a.max_blocks_per_seq, a.max_context_len);
-  const int nb = (L + kBlockTokens - 1) / kBlockTokens;
-  const int nparts = (nb + a.part_blocks - 1) / a.part_blocks;
-  if (nparts <= 1) return;
-  const size_t base = ((size_t)b * a.num_q_heads + hq) * a.max_parts;
-  const float* ml = a.ws_ml + base * 2;
-  const float* acc = a.ws_acc + base * D;
-  float M = neg_inf();
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  constexpr int PER = D / kWave;
-  float A[PER];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int h = lane * EPL / D, d0 = (lane * EPL) % D;
+  const size_t o = ((size_t)b * a.num_q_heads + (size_t)g * G + h) * D + d0;
+  const int c0 = a.prefix[b], nb = a.prefix[b + 1] - c0, total = a.prefix[a.batch];
+  if (nb == 0) {
+    if (wave == 0)
 #pragma unroll
-  for (int k = 0; k < PER; ++k) A[k] = 0.0f;
-  float Ls = 0.0f;
-  for (int p = 0; p < nparts; ++p) {
-    const float mp = ml[2 * p];
-    const float f = mp == neg_inf() ? 0.0f : fast_exp2(mp - M);
-    Ls = fmaf(ml[2 * p + 1], f, Ls);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) A[k] = fmaf(acc[(size_t)p * D + lane + kWave * k], f, A[k]);
+      for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, 0.0f);
+    return;
   }
-  const size_t o = ((size_t)b * a.num_q_heads + hq) * D;
+  const int NW = a.group_waves, HGC = a.num_kv_heads / NW;
+  const int hg = g / NW, wv = g % NW;
+  const int64_t T = (int64_t)HGC * total;
+  const int64_t S = (int64_t)HGC * c0 + (int64_t)hg * nb, E = S + nb - 1;
+  const ChunkGeom cg = chunk_geometry(T, a.num_ranges, a.part_units);
+  const int cf = chunk_of(cg, S), cl = chunk_of(cg, E);
+  if (cf == cl) return;                  // one chunk held the whole segment
+  // records of chunk c: its first piece is in slot 0, its last (if different) in slot
+  // 1; only chunk cf can hold the segment as its last piece. Empty chunks left none.
+  const int slot_f = chunk_begin(cg, cf) < S ? 1 : 0;
+  auto rec_of = [&](int c) -> size_t {
+    return (((size_t)c * 2 + (c == cf ? slot_f : 0)) * NW + wv) * G + h;
+  };
+
+  float M = neg_inf(), L = 0.0f, A[EPL];
 #pragma unroll
-  for (int k = 0; k < PER; ++k)
-    store_out<OT>(a.out, o + lane + kWave * k, Ls > 0.0f ? a.v_scale * (A[k] / Ls) : 0.0f);
+  for (int i = 0; i < EPL; ++i) A[i] = 0.0f;
+  for (int cb = cf + wave; cb <= cl; cb += MW * UNROLL) {
+    float mp[UNROLL], lp[UNROLL], x[UNROLL][EPL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int c = cb + u * MW;
+      const bool ok = c <= cl && chunk_begin(cg, c) < chunk_end(cg, c);
+      const size_t rec = rec_of(ok ? c : cf);
+      mp[u] = ok ? a.rec_ml[rec * 2] : neg_inf();
+      lp[u] = ok ? a.rec_ml[rec * 2 + 1] : 0.0f;
+      const float* src = a.rec_acc + rec * D + d0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[u][e] = ok ? src[e] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const float Mn = fmaxf(M, mp[u]);
+      if (Mn == neg_inf()) continue;     // nothing yet
+      const float sa = M == neg_inf() ? 0.0f : fast_exp2(M - Mn);
+      const float sb = mp[u] == neg_inf() ? 0.0f : fast_exp2(mp[u] - Mn);
+      L = L * sa + lp[u] * sb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) A[e] = A[e] * sa + x[u][e] * sb;
+      M = Mn;
+    }
+  }
+  if (d0 == 0) {
+    s_ml[wave][h][0] = M;
+    s_ml[wave][h][1] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_acc[wave][h * D + d0 + e] = A[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = neg_inf();
+#pragma unroll
+  for (int w = 0; w < MW; ++w) Mt = fmaxf(Mt, s_ml[w][h][0]);
+  float Lt = 0.0f, At[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) At[e] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) {
+    const float mw = s_ml[w][h][0];
+    const float f = mw == neg_inf() ? 0.0f : fast_exp2(mw - Mt);
+    Lt = fmaf(s_ml[w][h][1], f, Lt);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) At[e] = fmaf(s_acc[w][h * D + d0 + e], f, At[e]);
+  }
+  const float inv = Lt > 0.0f ? a.v_scale / Lt : 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, At[i] * inv);
 }
 
 template <int KV, int QT, int OT, int D, int G>
-hipError_t launch_decode_t(const DecodeArgs& args, int batch, hipStream_t stream) {
-  dim3 grid(args.num_kv_heads, batch, args.max_parts);
-  decode_kernel<KV, QT, OT, D, G, kDecodeWaves><<<grid, kDecodeWaves * kWave, 0, stream>>>(args);
+hipError_t launch_decode_t(const DecodeArgs& args, int nw, hipStream_t stream) {
+  decode_kernel<KV, QT, OT, D, G><<<dim3(args.num_ranges), dim3(nw * kWave), 0, stream>>>(args);
   return hipGetLastError();
 }
 
 template <int KV, int QT, int OT, int D>
-hipError_t dispatch_group(int group, const DecodeArgs& args, int batch, hipStream_t stream) {
+hipError_t dispatch_group(int group, const DecodeArgs& args, int nw, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_decode_t<KV, QT, OT, D, 1>(args, batch, stream);
-    case 2: return launch_decode_t<KV, QT, OT, D, 2>(args, batch, stream);
-    case 4: return launch_decode_t<KV, QT, OT, D, 4>(args, batch, stream);
-    case 8: return launch_decode_t<KV, QT, OT, D, 8>(args, batch, stream);
+    case 1: return launch_decode_t<KV, QT, OT, D, 1>(args, nw, stream);
+    case 2: return launch_decode_t<KV, QT, OT, D, 2>(args, nw, stream);
+    case 4: return launch_decode_t<KV, QT, OT, D, 4>(args, nw, stream);
+    case 8: return launch_decode_t<KV, QT, OT, D, 8>(args, nw, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int KV, int QT, int OT>
-hipError_t dispatch_dim(int head_dim, int group, const DecodeArgs& args, int batch,
+hipError_t dispatch_dim(int head_dim, int group, const DecodeArgs& args, int nw,
                         hipStream_t stream) {
   switch (head_dim) {
-    case 64: return dispatch_group<KV, QT, OT, 64>(group, args, batch, stream);
-    case 128: return dispatch_group<KV, QT, OT, 128>(group, args, batch, stream);
+    case 64: return dispatch_group<KV, QT, OT, 64>(group, args, nw, stream);
+    case 128: return dispatch_group<KV, QT, OT, 128>(group, args, nw, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int OT, int D>
+hipError_t launch_merge_t(int group, const MergeArgs& args, hipStream_t stream) {
+  const dim3 grid(args.num_kv_heads, args.batch), block(256);
+  switch (group) {
+    case 1: merge_kernel<OT, D, 1><<<grid, block, 0, stream>>>(args); break;
+    case 2: merge_kernel<OT, D, 2><<<grid, block, 0, stream>>>(args); break;
+    case 4: merge_kernel<OT, D, 4><<<grid, block, 0, stream>>>(args); break;
+    case 8: merge_kernel<OT, D, 8><<<grid, block, 0, stream>>>(args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(int q_dtype, int kv_dtype, int out_dtype, int head_dim, int group,
-                         const DecodeArgs& args, int batch, hipStream_t stream) {
+                         const DecodeArgs& args, int nw, hipStream_t stream) {
   if (q_dtype == PA_F32 && kv_dtype == PA_F32 && out_dtype == PA_F32)
-    return dispatch_dim<PA_F32, PA_F32, PA_F32>(head_dim, group, args, batch, stream);
+    return dispatch_dim<PA_F32, PA_F32, PA_F32>(head_dim, group, args, nw, stream);
   if (q_dtype == PA_F16 && kv_dtype == PA_F16) {
     if (out_dtype == PA_F16)
-      return dispatch_dim<PA_F16, PA_F16, PA_F16>(head_dim, group, args, batch, stream);
+      return dispatch_dim<PA_F16, PA_F16, PA_F16>(head_dim, group, args, nw, stream);
     if (out_dtype == PA_F32)
-      return dispatch_dim<PA_F16, PA_F16, PA_F32>(head_dim, group, args, batch, stream);
+      return dispatch_dim<PA_F16, PA_F16, PA_F32>(head_dim, group, args, nw, stream);
   }
   if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) {
     if (out_dtype == PA_BF16)
-      return dispatch_dim<PA_BF16, PA_BF16, PA_BF16>(head_dim, group, args, batch, stream);
+      return dispatch_dim<PA_BF16, PA_BF16, PA_BF16>(head_dim, group, args, nw, stream);
     if (out_dtype == PA_F32)
-      return dispatch_dim<PA_BF16, PA_BF16, PA_F32>(head_dim, group, args, batch, stream);
+      return dispatch_dim<PA_BF16, PA_BF16, PA_F32>(head_dim, group, args, nw, stream);
   }
   if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3) {
     if (out_dtype == PA_BF16)
-      return dispatch_dim<PA_FP8_E4M3, PA_BF16, PA_BF16>(head_dim, group, args, batch, stream);
+      return dispatch_dim<PA_FP8_E4M3, PA_BF16, PA_BF16>(head_dim, group, args, nw, stream);
     if (out_dtype == PA_F32)
-      return dispatch_dim<PA_FP8_E4M3, PA_BF16, PA_F32>(head_dim, group, args, batch, stream);
+      return dispatch_dim<PA_FP8_E4M3, PA_BF16, PA_F32>(head_dim, group, args, nw, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(int out_dtype, int head_dim, const MergeArgs& args, int batch,
+hipError_t launch_merge(int out_dtype, int head_dim, int group, const MergeArgs& args,
                         hipStream_t stream) {
-  dim3 grid((args.num_q_heads + 3) / 4, batch);
-  dim3 block(256);
-#define PA_MERGE(OT, D) merge_kernel<OT, D><<<grid, block, 0, stream>>>(args)
   if (head_dim == 64) {
-    if (out_dtype == PA_F32) PA_MERGE(PA_F32, 64);
-    else if (out_dtype == PA_F16) PA_MERGE(PA_F16, 64);
-    else PA_MERGE(PA_BF16, 64);
-  } else {
-    if (out_dtype == PA_F32) PA_MERGE(PA_F32, 128);
-    else if (out_dtype == PA_F16) PA_MERGE(PA_F16, 128);
-    else PA_MERGE(PA_BF16, 128);
+    if (out_dtype == PA_F32) return launch_merge_t<PA_F32, 64>(group, args, stream);
+    if (out_dtype == PA_F16) return launch_merge_t<PA_F16, 64>(group, args, stream);
+    return launch_merge_t<PA_BF16, 64>(group, args, stream);
   }
-#undef PA_MERGE
-  return hipGetLastError();
+  if (out_dtype == PA_F32) return launch_merge_t<PA_F32, 128>(group, args, stream);
+  if (out_dtype == PA_F16) return launch_merge_t<PA_F16, 128>(group, args, stream);
+  return launch_merge_t<PA_BF16, 128>(group, args, stream);
 }
 
 }  // namespace pa

@@ -8,12 +8,56 @@
 namespace pa {
 
 constexpr int kBlockTokens = 16;      // tokens per KV block (the only supported size)
-constexpr int kDecodeWaves = 4;       // waves per decode workgroup
-constexpr int kMaxPartitionTokens = 4096;
-constexpr int kDefaultPartitionTokens = 512;
+constexpr int kMaxGroupWaves = 8;     // waves per decode workgroup (= kv heads per head group)
+constexpr int kDeviceCUs = 256;       // compute units of an MI355X (gfx950)
+constexpr int kWavesPerCU = 8;        // decode registers are sized for 2 waves per SIMD
+constexpr int kMaxPartitionTokens = 1 << 20;
+constexpr int kMaxBatch = 4096;       // lengths and prefix sums of the batch sit in LDS
 
-// Arguments of the split-KV decode kernel. One workgroup handles one
-// (partition, kv head, sequence) triple.
+// Work split of one decode call. A unit is one 16-token block of one sequence for one
+// head group (kv heads hg*NW .. hg*NW + NW - 1). Units are numbered sequence-major, then
+// head group, then logical block, so each (sequence, head group) is a contiguous segment
+// of nb = ceil(L / 16) units. There are T = (Hkv / NW) * sum_b nb units, cut into chunks;
+// a workgroup of NW waves (one per kv head of the group) walks its chunks unit by unit.
+// A segment cut by a chunk boundary leaves one (m, l, acc) record per piece, which
+// merge_kernel combines; a segment inside one chunk is written out directly.
+//
+// Chunks of [0, T), numbered in unit order. Default: W static chunks, chunk r =
+// [T*r/W, T*(r+1)/W), one per workgroup (a chunk may be empty when T < W). With a fixed
+// partition of P blocks: nsmall chunks of P units (the last may be shorter), numbered
+// from W and taken from a counter by whichever workgroup is free.
+struct ChunkGeom {
+  int64_t T, C2;
+  int W, nsmall;
+  bool fixed;
+};
+constexpr int64_t kMaxChunks = 16384;
+
+__host__ __device__ inline ChunkGeom chunk_geometry(int64_t T, int W, int fixed_units) {
+  ChunkGeom g;
+  g.T = T;
+  g.W = W;
+  g.fixed = fixed_units > 0;
+  g.C2 = g.fixed ? fixed_units : 1;
+  g.nsmall = g.fixed ? (int)((T + fixed_units - 1) / fixed_units) : 0;
+  return g;
+}
+__host__ __device__ inline int64_t chunk_begin(const ChunkGeom& g, int c) {
+  if (c < g.W) return g.fixed ? 0 : g.T * c / g.W;
+  return (int64_t)(c - g.W) * g.C2;
+}
+__host__ __device__ inline int64_t chunk_end(const ChunkGeom& g, int c) {
+  if (c < g.W) return g.fixed ? 0 : g.T * (c + 1) / g.W;
+  const int64_t e = chunk_begin(g, c) + g.C2;
+  return e > g.T ? g.T : e;
+}
+// chunk holding unit u (0 <= u < T): the last static chunk starting at or before u, or
+// the taken chunk u / P
+__host__ __device__ inline int chunk_of(const ChunkGeom& g, int64_t u) {
+  if (g.fixed) return g.W + (int)(u / g.C2);
+  return (int)(((u + 1) * g.W - 1) / g.T);
+}
+
 struct DecodeArgs {
   void* out;                    // [B, Hq, d] out dtype
   const void* q;                // [B, Hq, d] q dtype
@@ -21,36 +65,47 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_tables;  // [B, maxb]
   const int32_t* context_lens;  // [B]
-  float* ws_acc;                // [B, Hq, max_parts, d]   (only when max_parts > 1)
-  float* ws_ml;                 // [B, Hq, max_parts, 2]   (m in log2 units, l)
+  int32_t* counters;            // [2] small chunks taken, workgroups done (zero between calls)
+  float* rec_acc;               // [chunks, 2, NW, G, d]  unnormalised partial outputs
+  float* rec_ml;                // [chunks, 2, NW, G, 2]  (running max m in log2 units, sum l)
+  int32_t* prefix;              // [B + 1] blocks before each sequence (workgroup 0 writes)
+  int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t part_blocks;          // blocks per partition
-  int32_t max_parts;            // partitions covering max_context_len
+  int32_t num_ranges;           // W, workgroups
+  int32_t part_units;           // fixed chunk length in units, 0 = default split
   float qk_scale_log2;          // scale * k_scale * log2(e)
   float v_scale;
 };
 
-// Arguments of the cross-partition merge kernel. One wave per (sequence, query head).
+// Arguments of the merge kernel: one wave per (kv head, sequence).
 struct MergeArgs {
   void* out;
-  const int32_t* context_lens;
-  const float* ws_acc;
-  const float* ws_ml;
+  const float* rec_acc;
+  const float* rec_ml;
+  const int32_t* prefix;
+  int32_t batch;
   int32_t num_q_heads;
-  int32_t max_blocks_per_seq;
-  int32_t max_context_len;
-  int32_t part_blocks;
-  int32_t max_parts;
+  int32_t num_kv_heads;
+  int32_t group_waves;          // NW
+  int32_t num_ranges;           // W
+  int32_t part_units;
   float v_scale;
 };
 
+// Waves per workgroup for Hkv kv heads: the largest of 8, 4, 2, 1 dividing Hkv.
+inline int group_waves(int num_kv_heads) {
+  for (int nw = kMaxGroupWaves; nw > 1; nw >>= 1)
+    if (num_kv_heads % nw == 0) return nw;
+  return 1;
+}
+
 hipError_t launch_decode(int q_dtype, int kv_dtype, int out_dtype, int head_dim, int group,
-                         const DecodeArgs& args, int batch, hipStream_t stream);
-hipError_t launch_merge(int out_dtype, int head_dim, const MergeArgs& args, int batch,
+                         const DecodeArgs& args, int group_waves, hipStream_t stream);
+hipError_t launch_merge(int out_dtype, int head_dim, int group, const MergeArgs& args,
                         hipStream_t stream);
 
 hipError_t launch_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,

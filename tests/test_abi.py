@@ -56,25 +56,44 @@ def _decode(lib, desc, max_ctx=8192, ptr=0x10000, ws=None, ws_bytes=0, scale=0.0
                          max_ctx, scale, 1.0, 1.0, ws, ws_bytes, None)
 
 
-def test_partition_and_workspace_sizes(lib):
+def _ws_bytes(chunks, nw, G, d, B):
+    up = lambda x: (x + 255) // 256 * 256
+    recs = chunks * 2 * nw * G
+    return 256 + up(recs * d * 4) + up(recs * 2 * 4) + up((B + 1) * 4)
+
+
+def test_chunks_and_workspace_sizes(lib):
     d = _desc()
-    assert pa.pa_decode_partition_size(d, 8192) == 512
-    mp = 8192 // 512
-    acc = 256 * 32 * mp * 128 * 4
-    assert pa.pa_decode_workspace_bytes(d, 8192) == acc + 256 * 32 * mp * 2 * 4
-    assert pa.pa_decode_workspace_bytes(d, 512) == 0          # one partition: no workspace
-    d.partition_size = 1024
-    assert pa.pa_decode_partition_size(d, 8192) == 1024
+    # default: one static chunk per workgroup; 256 workgroups of 8 waves (8 waves per CU
+    # on 256 CUs)
+    assert pa.pa_decode_max_chunks(d, 8192) == 256
+    assert pa.pa_decode_workspace_bytes(d, 8192) == _ws_bytes(256, 8, 4, 128, 256)
+    assert pa.pa_decode_workspace_bytes(d, 16) == _ws_bytes(256, 8, 4, 128, 256)
+    # fixed partitions of 512 tokens: every 32-block partition of 256 x 512 blocks
+    d.partition_size = 512
+    assert pa.pa_decode_max_chunks(d, 8192) == 256 + 256 * 512 // 32
     d.partition_size = 100                                     # not a multiple of 16
-    assert pa.pa_decode_partition_size(d, 8192) == -4
+    assert pa.pa_decode_max_chunks(d, 8192) == -4
     assert pa.pa_decode_workspace_bytes(d, 8192) == 0
+    d.partition_size = 16                                      # 131072 chunks: too many
+    assert pa.pa_decode_max_chunks(d, 8192) == -4
+    # 32 kv heads (MHA): still 8 per workgroup; 4 kv heads: 4 waves, 512 workgroups
+    d = _desc(num_q_heads=32, num_kv_heads=32)
+    assert pa.pa_decode_max_chunks(d, 8192) == 256
+    d = _desc(num_q_heads=16, num_kv_heads=4)
+    assert pa.pa_decode_max_chunks(d, 8192) == 512
+    assert pa.pa_decode_workspace_bytes(d, 8192) == _ws_bytes(512, 4, 4, 128, 256)
+    d = _desc(num_q_heads=12, num_kv_heads=6)                 # 6 kv heads: 2 per workgroup
+    assert pa.pa_decode_max_chunks(d, 8192) == 1024
+    assert pa.pa_decode_workspace_bytes(_desc(batch=0), 8192) == 0
 
 
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, -4), ("block_size", 32, -4), ("num_q_heads", 30, -2),
     ("num_q_heads", 8 * 16, -4), ("q_dtype", 7, -3), ("kv_dtype", -1, -3),
     ("out_dtype", pa.PA_F16, -4), ("num_blocks", 0, -2), ("batch", -1, -2),
-    ("partition_size", 8192, -4), ("max_blocks_per_seq", 0, -2),
+    ("partition_size", 8200, -4), ("partition_size", 1 << 21, -4),
+    ("max_blocks_per_seq", 0, -2), ("batch", 4097, -4),
 ])
 def test_decode_rejects_bad_descriptor(lib, field, value, code):
     d = _desc(**{field: value})
@@ -87,6 +106,7 @@ def test_decode_rejects_before_launch(lib):
     assert _decode(lib, _desc(), ptr=0) == -1                        # null arrays
     assert _decode(lib, _desc(), ptr=0x10008) == -6                  # misaligned
     assert _decode(lib, _desc(), ws=None, ws_bytes=0) == -5          # workspace needed
+    assert _decode(lib, _desc(batch=4), max_ctx=16, ws=None) == -5   # even for short ones
     assert _decode(lib, _desc(), ws=ctypes.c_void_p(0x20000), ws_bytes=16) == -5
     assert _decode(lib, _desc(), scale=float("nan")) == -2
     assert _decode(lib, _desc(batch=0)) == 0                         # empty batch: no-op
