@@ -59,6 +59,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x1 __attribute__((ext_vector_type(1)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -128,6 +131,14 @@ template <> struct VChunk<8> {
     return buf_load8(r, o);
   }
 };
+template <> struct VChunk<4> {
+  using type = u32x1;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    u32x1 v;
+    v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, 0);
+    return v;
+  }
+};
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
@@ -144,6 +155,51 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
     static_cast<_Float16*>(out)[idx] = (_Float16)x;
   } else {
     static_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(x);
+  }
+}
+
+// Matrix-core P.V (16-bit and fp8 K/V). V words of one token row, as pairs of 16-bit values
+// in the MFMA's element type (fp8 widened exactly to bf16).
+template <int KV, int WORDS, typename VTy>
+__device__ __forceinline__ void v_words16(const VTy& w, uint32_t (&o)[WORDS]) {
+  if constexpr (KV == PA_FP8_E4M3) {
+#pragma unroll
+    for (int i = 0; i < WORDS / 2; ++i) {
+      o[2 * i] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t,
+                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) o[i] = w[i];
+  }
+}
+// One 16x16x16 MFMA in the element type of KV (fp16 for fp16, bf16 otherwise).
+template <int KV>
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (KV == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+// p rounded to the MFMA element type (kept in fp32), and two such values packed.
+template <int KV>
+__device__ __forceinline__ float round16(float x) {
+  if constexpr (KV == PA_F16) return (float)(_Float16)x;
+  else return __uint_as_float((uint32_t)f32_to_bf16_rne(x) << 16);
+}
+template <int KV>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (KV == PA_F16) {
+    const uint32_t l = __builtin_bit_cast(uint16_t, (_Float16)lo);
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)hi);
+    return l | h << 16;
+  } else {
+    // exact: both values were rounded to bf16 already
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
   }
 }
 
@@ -257,11 +313,15 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   constexpr int ROWB = D * KB;            // bytes of one token's K (or V) row, one kv head
   constexpr int NL = ROWB / 64;           // K: 16-byte loads per lane per block
   constexpr int EPC = 16 / KB;            // K: elements per 16-byte chunk
-  // V stage: each lane loads VB-byte pieces (8 for fp8, so that a lane's accumulators
-  // stay at 8 elements per head), LPR lanes per token row, RPI rows per instruction
-  constexpr int VB = KB == 1 ? 8 : 16;
-  constexpr int VEPC = VB / KB;
-  constexpr int LPR = ROWB / VB;
+  // P.V runs on the matrix cores for 16-bit and fp8 K/V (MPV): lane (n, kq) = (lane % 16,
+  // lane / 16) loads DPL dims (DPL*n ..) of tokens 4kq .. 4kq+3, one token per load, so
+  // the 16x16x16 MFMA's B operand for dim DPL*n + e is two byte permutes away. fp32 K/V
+  // keeps P.V on the vector ALU: lane (r, c) loads 16-byte chunk c of rows r, r + RPI, ...
+  constexpr bool MPV = KV != PA_F32;
+  constexpr int DPL = D / 16;
+  constexpr int VB = MPV ? DPL * KB : 16;  // V bytes per lane per load
+  constexpr int VEPC = VB / KB;            // V elements per lane per load
+  constexpr int LPR = MPV ? 16 : ROWB / VB;
   constexpr int RPI = kWave / LPR;
   constexpr int NLV = kBlockTokens / RPI; // V: loads per lane per block
   using VT = typename VChunk<VB>::type;
@@ -277,12 +337,12 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   // the 256 registers of 2 waves per SIMD next to the accumulators and q operand
   constexpr int BLK_WAVE_BYTES = (NL * 16 + NLV * VB) * kWave;  // K + V of one block, one wave
   constexpr int SLOT_VGPRS = NL * 4 + NLV * (VB / 4) + QPL * 4 + 1;
-  constexpr int FIXED_VGPRS = G * VEPC + NL * QCH * 4 + 2 * G + 80;
+  constexpr int FIXED_VGPRS = (MPV ? DPL * 4 : G * VEPC) + NL * QCH * 4 + 2 * G + 80;
   constexpr int NBUF_FIT = (256 - FIXED_VGPRS) / SLOT_VGPRS - 1;
   constexpr int NBUF_BYTES = kRingBytes / BLK_WAVE_BYTES;
   constexpr int NBUF_MIN = NBUF_BYTES < NBUF_FIT ? NBUF_BYTES : NBUF_FIT;
   constexpr int NBUF = NBUF_MIN < 1 ? 1 : (NBUF_MIN > 3 ? 3 : NBUF_MIN);
-  constexpr int PBUF = kBlockTokens * G + 8;    // p[16][G] + alpha[8], one block, one wave
+  constexpr int PBUF = kBlockTokens * G + 8;    // p of one block (+ alpha[8]), one wave
 
   __shared__ int s_lens[kMaxBatch];        // clamped context length per sequence
   __shared__ int s_pre[kMaxBatch + 1];     // blocks before each sequence
@@ -447,7 +507,9 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   const uint8_t* const qbase = static_cast<const uint8_t*>(a.q);
   // per-lane byte offsets inside one kv head's slice of a block (constant)
   const uint32_t koff = (lane & 15) * tok_stride + (lane >> 4) * 16;
-  const uint32_t voff = (lane / LPR) * tok_stride + (lane % LPR) * VB;
+  const uint32_t voff = MPV ? (4 * (lane >> 4)) * tok_stride + (lane & 15) * VB
+                            : (lane / LPR) * tok_stride + (lane % LPR) * VB;
+  const uint32_t vstep = MPV ? tok_stride : RPI * tok_stride;   // between a lane's V loads
 
   // physical id of a unit's block (every lane reads the same word); zero-size descriptor
   // for units past the range, so the load costs nothing
@@ -476,13 +538,14 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NL; ++s) kb[s] = buf_load16(rk, koff + s * 64);
 #pragma unroll
-    for (int i = 0; i < NLV; ++i) vb[i] = VChunk<VB>::load(rv, voff + i * RPI * tok_stride);
+    for (int i = 0; i < NLV; ++i) vb[i] = VChunk<VB>::load(rv, voff + i * vstep);
   };
 
   // ---- 4. running state of the current piece
   u32x4 qreg[NL][QCH];
   float m[HPL], lsum[HPL];
-  float acc[G][VEPC];
+  float acc[G][VEPC];                      // vector-ALU P.V: lane (r, c), all G heads
+  f32x4 acc4[DPL];                         // matrix-core P.V: dim DPL*n + e, rows 4kq + v
   bool piece_whole_start = false;          // the current piece began at its segment's start
   int piece_slot = 0;
   float* const pw = &s_p[wave][0];
@@ -500,10 +563,15 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
         m[r] = neg_inf();
         lsum[r] = 0.0f;
       }
+      if constexpr (MPV) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+        for (int e = 0; e < DPL; ++e) acc4[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      } else {
 #pragma unroll
-        for (int e = 0; e < VEPC; ++e) acc[h][e] = 0.0f;
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < VEPC; ++e) acc[h][e] = 0.0f;
+      }
 #pragma unroll
       for (int i = 0; i < QPL; ++i)
         if ((lane + kWave * i) * 16 < QBYTES)
@@ -536,21 +604,68 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       al[r] = mn == neg_inf() ? 1.0f : fast_exp2(m[r] - mn);
       p[r] = fast_exp2(s - mn);
       if (ragged) p[r] = tok_ok ? p[r] : 0.0f;
+      // the matrix cores take p in 16 bits; l sums the same rounded weights, so the
+      // output stays an exact weighted average of the V rows
+      if constexpr (MPV) p[r] = round16<KV>(p[r]);
       lsum[r] = lsum[r] * al[r] + p[r];
       m[r] = mn;
     }
     if ((lane >> 4) < QROWS) {
       const int hb = G > 4 ? 4 * (lane >> 4) : 0;
-      float* dst = P + (lane & 15) * G + hb;
+      if constexpr (MPV) {
+        // head-major: P[h][t]
 #pragma unroll
-      for (int r = 0; r < HPL; ++r) dst[r] = p[r];
-      if constexpr (G > 4) {
-        if ((lane & 15) == 0)
+        for (int r = 0; r < HPL; ++r) P[(hb + r) * kBlockTokens + (lane & 15)] = p[r];
+      } else {
+        float* dst = P + (lane & 15) * G + hb;
 #pragma unroll
-          for (int r = 0; r < HPL; ++r) P[kBlockTokens * G + hb + r] = al[r];
+        for (int r = 0; r < HPL; ++r) dst[r] = p[r];
+        if constexpr (G > 4) {
+          if ((lane & 15) == 0)
+#pragma unroll
+            for (int r = 0; r < HPL; ++r) P[kBlockTokens * G + hb + r] = al[r];
+        }
       }
     }
     wave_lds_sync();
+
+    if constexpr (MPV) {
+      // rescale: accumulator rows 4kq + v belong to head (4kq + v) % G, whose factor this
+      // lane computed as al[v % HPL] (same row group in the QK^T and P.V layouts)
+      bool moved = false;
+#pragma unroll
+      for (int r = 0; r < HPL; ++r) moved |= al[r] != 1.0f;
+      if (moved) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc4[e][v] *= al[v % HPL];
+      }
+      // A operand: p of tokens 4kq .. 4kq+3 for head (lane % 16) % G
+      const f32x4 pp =
+          *reinterpret_cast<const f32x4*>(P + ((lane & 15) % G) * kBlockTokens + 4 * (lane >> 4));
+      const u32x2 aop = {pack16<KV>(pp[0], pp[1]), pack16<KV>(pp[2], pp[3])};
+      // B operands: token rows 4kq + i of this lane's dims; rows at or past L are zeroed
+      // (their p is 0, but the slot may hold NaN)
+      constexpr int WORDS = DPL / 2;
+      uint32_t vw[4][WORDS];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v_words16<KV, WORDS>(vb[i], vw[i]);
+        if (ragged) {
+          const bool ok = 4 * (lane >> 4) + i < rem;
+#pragma unroll
+          for (int w = 0; w < WORDS; ++w) vw[i][w] = ok ? vw[i][w] : 0u;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 bop = {__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
+                           __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel)};
+        acc4[e] = mfma16<KV>(aop, bop, acc4[e]);
+      }
+    } else {
 
     float alpha[G];
     if constexpr (G > 4) {
@@ -588,53 +703,82 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < VEPC; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
     }
+    }   // vector-ALU P.V
 
     if (!(fl & kLast)) return;
     // ---- the piece ends here: reduce over lanes, then write the output (whole segment)
-    // or a record (a piece of a segment cut by a range boundary)
+    // or a record (a piece of a segment cut by a chunk boundary)
 #pragma unroll
     for (int r = 0; r < HPL; ++r) lsum[r] = row16_sum(lsum[r]);
+    const bool whole = piece_whole_start && (fl & kSegEnd);
+    const size_t rec = ((size_t)mu.chunk() * 2 + piece_slot) * NW + wave;
+    if constexpr (MPV) {
+      // every row group holds the full sums; lanes of row group kq < QROWS write heads
+      // hb + v (v < HPL) for dims DPL*n + e, with their own m and l
+      if ((lane >> 4) < QROWS) {
+        const int hb = G > 4 ? 4 * (lane >> 4) : 0;
+        const int n = lane & 15;
 #pragma unroll
-    for (int st = LPR; st < kWave; st <<= 1)
+        for (int v = 0; v < HPL; ++v) {
+          const int h = hb + v;
+          if (whole) {
+            const size_t o = ((size_t)mu.b() * Hq + (size_t)g * G + h) * D + DPL * n;
+            const float inv = lsum[v] > 0.0f ? a.v_scale / lsum[v] : 0.0f;
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+            for (int e = 0; e < DPL; ++e) store_out<OT>(a.out, o + e, acc4[e][v] * inv);
+          } else {
 #pragma unroll
-        for (int e = 0; e < VEPC; ++e) acc[h][e] += __shfl_xor(acc[h][e], st);
-    float mh[G], lh[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if constexpr (G > 4) {
-        mh[h] = __shfl(m[h & 3], (h >> 2) * 16);
-        lh[h] = __shfl(lsum[h & 3], (h >> 2) * 16);
-      } else {
-        mh[h] = m[h];
-        lh[h] = lsum[h];
-      }
-    }
-    if (piece_whole_start && (fl & kSegEnd)) {
-      if (lane < LPR) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const size_t o = ((size_t)mu.b() * Hq + (size_t)g * G + h) * D + VEPC * lane;
-          const float inv = lh[h] > 0.0f ? a.v_scale / lh[h] : 0.0f;
-#pragma unroll
-          for (int e = 0; e < VEPC; ++e) store_out<OT>(a.out, o + e, acc[h][e] * inv);
+            for (int e = 0; e < DPL; ++e)
+              a.rec_acc[(rec * G + h) * D + DPL * n + e] = acc4[e][v];
+            if (n == 0) {
+              a.rec_ml[(rec * G + h) * 2] = m[v];
+              a.rec_ml[(rec * G + h) * 2 + 1] = lsum[v];
+            }
+          }
         }
       }
     } else {
-      const size_t rec = ((size_t)mu.chunk() * 2 + piece_slot) * NW + wave;
-      if (lane < LPR) {
+#pragma unroll
+      for (int st = LPR; st < kWave; st <<= 1)
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < VEPC; ++e)
-            a.rec_acc[(rec * G + h) * D + VEPC * lane + e] = acc[h][e];
-      }
+          for (int e = 0; e < VEPC; ++e) acc[h][e] += __shfl_xor(acc[h][e], st);
+      float mh[G], lh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        if (lane == h) {
-          a.rec_ml[(rec * G + h) * 2] = mh[h];
-          a.rec_ml[(rec * G + h) * 2 + 1] = lh[h];
+        if constexpr (G > 4) {
+          mh[h] = __shfl(m[h & 3], (h >> 2) * 16);
+          lh[h] = __shfl(lsum[h & 3], (h >> 2) * 16);
+        } else {
+          mh[h] = m[h];
+          lh[h] = lsum[h];
+        }
+      }
+      if (whole) {
+        if (lane < LPR) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const size_t o = ((size_t)mu.b() * Hq + (size_t)g * G + h) * D + VEPC * lane;
+            const float inv = lh[h] > 0.0f ? a.v_scale / lh[h] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEPC; ++e) store_out<OT>(a.out, o + e, acc[h][e] * inv);
+          }
+        }
+      } else {
+        if (lane < LPR) {
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < VEPC; ++e)
+              a.rec_acc[(rec * G + h) * D + VEPC * lane + e] = acc[h][e];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (lane == h) {
+            a.rec_ml[(rec * G + h) * 2] = mh[h];
+            a.rec_ml[(rec * G + h) * 2 + 1] = lh[h];
+          }
         }
       }
     }

@@ -65,6 +65,13 @@ def test_partition_sizes(part):
     _check(w, gpu_decode(w, d, partition_size=part), oracle_decode(w))
 
 
+# The matrix cores take the softmax weights p in 16 bits: fp16 for fp16 K/V (relative
+# rounding 2^-11), bf16 otherwise (2^-8 at most, 2^-9 typically). The normaliser sums the
+# same rounded weights, so the output stays a weighted average of V rows whose weights are
+# off by that much: the error is a fraction 2^-9 .. 2^-11 of the spread |v - out|.
+FP32_OUT_TOL = {"f16": 2e-3, "bf16": 5e-3, "fp8_e4m3": 5e-3}
+
+
 @pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3"])
 def test_fp32_output_tightens_error(kv):
     """With an fp32 output the only error left is the kernel's own arithmetic."""
@@ -72,7 +79,7 @@ def test_fp32_output_tightens_error(kv):
                   context_lens=[3, 64, 400, 777, 1500], seed=7)
     dev = to_device(w)
     out = gpu_decode(w, dev, out_dtype="f32")
-    _check(w, out, oracle_decode(w), tol=2e-3)
+    _check(w, out, oracle_decode(w), tol=FP32_OUT_TOL[kv])
 
 
 def test_nan_in_unused_slots_changes_nothing():
