@@ -98,6 +98,11 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// A value the whole wave agrees on (an LDS word read at a uniform address), marked as
+// such so that what is derived from it stays in scalar registers; without this the
+// compiler wraps every load whose descriptor depends on it in a per-lane loop.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Make LDS writes of this wave visible to its own later LDS reads from other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   // uniform within a wave; say so, so that everything derived stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int B = a.batch, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  const int HGC = Hkv / NW;                          // head groups
+  const int HGC = uni(Hkv / NW);                     // head groups
   const int cap = min(a.max_blocks_per_seq * kBlockTokens, a.max_context_len);
 
   // ---- 1. lengths and block prefix sums of the whole batch, in LDS. Thread t owns the
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   int before = 0, total = 0;
   for (int w = 0; w < NW; ++w) {
-    const int x = s_wsum[w];
+    const int x = uni(s_wsum[w]);
     before += w < wave ? x : 0;
     total += x;
   }
@@ -421,14 +426,14 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (HGC * s_pre[mid] <= u) lo = mid;
+      if (HGC * uni(s_pre[mid]) <= u) lo = mid;
       else hi = mid - 1;
     }
     wb = lo;
-    wL = s_lens[lo];
+    wL = uni(s_lens[lo]);
     wnb = nblocks(wL);
-    const int rel = u - HGC * s_pre[lo];
-    whg = rel / wnb;
+    const int rel = u - HGC * uni(s_pre[lo]);
+    whg = uni(rel / wnb);   // integer division runs on the vector ALU
     wj = rel - whg * wnb;
   };
   // Ask for the chunk after the current one. atomicInc (increment with a wrap bound that
@@ -440,8 +445,8 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   auto enter = [&](int c) {
     cur = c;
     if (c < 0) return;
-    cbeg = (int)chunk_begin(cg, c);
-    cend = (int)chunk_end(cg, c);
+    cbeg = uni((int)chunk_begin(cg, c));
+    cend = uni((int)chunk_end(cg, c));
     wu = cbeg;
     locate(wu);
     grab();
@@ -478,9 +483,9 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       if (wu == cend - 1) f |= kLast;
     }
     const int rem = min(kBlockTokens, wL - wj * kBlockTokens);
-    m.bf = wb | f << 16 | (rem > 0 ? rem : 0) << 24;
-    m.j = wj;
-    m.hc = whg | (cur >= 0 ? cur : 0) << 12;
+    m.bf = uni(wb | f << 16 | (rem > 0 ? rem : 0) << 24);
+    m.j = uni(wj);
+    m.hc = uni(whg | (cur >= 0 ? cur : 0) << 12);
     return m;
   };
   auto advance = [&]() {
@@ -495,7 +500,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     whg = 0;
     do {                  // wu < cend guarantees a non-empty sequence follows
       ++wb;
-      wL = s_lens[wb];
+      wL = uni(s_lens[wb]);
       wnb = nblocks(wL);
     } while (wnb == 0 && wb + 1 < B);
   };
