@@ -81,15 +81,47 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror: after the four
-// steps every lane of a 16-lane row holds the row's reduction.
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
-  x = fmaxf(x, dpp<0x141>(x));
-  x = fmaxf(x, dpp<0x140>(x));
-  return x;
+// Row reductions use four DPP steps, quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror and row_mirror: after them every lane of a 16-lane row holds the
+// row's result.
+//
+// Row maxima of N independent values per lane (N = 1, 2, 4), in place: v_max_f32 with a
+// DPP source over the same four steps. The N chains are interleaved so that each DPP
+// source was written at least two wait states earlier (s_nop fills the rest), and the
+// fused form skips the separate move and the NaN-quieting max the compiler adds.
+#define PA_DPPMAX(i, ctl) "v_max_f32_dpp %" #i ", %" #i ", %" #i " " ctl " row_mask:0xf bank_mask:0xf\n"
+#define PA_Q1 "quad_perm:[1,0,3,2]"
+#define PA_Q2 "quad_perm:[2,3,0,1]"
+#define PA_HM "row_half_mirror"
+#define PA_MI "row_mirror"
+template <int N>
+__device__ __forceinline__ void row16_max_n(float (&x)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 rows");
+  if constexpr (N == 4) {
+    asm volatile("s_nop 1\n"
+                 PA_DPPMAX(0, PA_Q1) PA_DPPMAX(1, PA_Q1) PA_DPPMAX(2, PA_Q1) PA_DPPMAX(3, PA_Q1)
+                 PA_DPPMAX(0, PA_Q2) PA_DPPMAX(1, PA_Q2) PA_DPPMAX(2, PA_Q2) PA_DPPMAX(3, PA_Q2)
+                 PA_DPPMAX(0, PA_HM) PA_DPPMAX(1, PA_HM) PA_DPPMAX(2, PA_HM) PA_DPPMAX(3, PA_HM)
+                 PA_DPPMAX(0, PA_MI) PA_DPPMAX(1, PA_MI) PA_DPPMAX(2, PA_MI) PA_DPPMAX(3, PA_MI)
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+  } else if constexpr (N == 2) {
+    asm volatile("s_nop 1\n"
+                 PA_DPPMAX(0, PA_Q1) PA_DPPMAX(1, PA_Q1) "s_nop 0\n"
+                 PA_DPPMAX(0, PA_Q2) PA_DPPMAX(1, PA_Q2) "s_nop 0\n"
+                 PA_DPPMAX(0, PA_HM) PA_DPPMAX(1, PA_HM) "s_nop 0\n"
+                 PA_DPPMAX(0, PA_MI) PA_DPPMAX(1, PA_MI)
+                 : "+v"(x[0]), "+v"(x[1]));
+  } else {
+    asm volatile("s_nop 1\n" PA_DPPMAX(0, PA_Q1) "s_nop 1\n" PA_DPPMAX(0, PA_Q2)
+                 "s_nop 1\n" PA_DPPMAX(0, PA_HM) "s_nop 1\n" PA_DPPMAX(0, PA_MI)
+                 : "+v"(x[0]));
+  }
 }
+#undef PA_DPPMAX
+#undef PA_Q1
+#undef PA_Q2
+#undef PA_HM
+#undef PA_MI
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<0xB1>(x);
   x += dpp<0x4E>(x);
@@ -145,11 +177,9 @@ template <> struct VChunk<4> {
   }
 };
 
+// fp32 -> bf16, round to nearest even (the hardware conversion of CDNA4)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 template <int OT>
@@ -600,20 +630,23 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NL; ++s) sc = qk_chunk<KV>(sc, kb[s], qreg[s]);
     const bool tok_ok = (lane & 15) < rem;
-    float al[HPL], p[HPL];
+    // (tok_ok holds on every lane of a full block, so the masks need no branch)
+    float al[HPL], p[HPL], sv[HPL], mn[HPL];
 #pragma unroll
     for (int r = 0; r < HPL; ++r) {
-      float s = sc[r] * a.qk_scale_log2;
-      if (ragged) s = tok_ok ? s : neg_inf();
-      const float mn = fmaxf(m[r], row16_max(s));
-      al[r] = mn == neg_inf() ? 1.0f : fast_exp2(m[r] - mn);
-      p[r] = fast_exp2(s - mn);
-      if (ragged) p[r] = tok_ok ? p[r] : 0.0f;
+      sv[r] = tok_ok ? sc[r] * a.qk_scale_log2 : neg_inf();
+      mn[r] = sv[r] > m[r] ? sv[r] : m[r];   // m is the same on all lanes of a row
+    }
+    row16_max_n<HPL>(mn);                  // new running maxima, one per head
+#pragma unroll
+    for (int r = 0; r < HPL; ++r) {
+      al[r] = mn[r] == neg_inf() ? 1.0f : fast_exp2(m[r] - mn[r]);
+      p[r] = tok_ok ? fast_exp2(sv[r] - mn[r]) : 0.0f;
       // the matrix cores take p in 16 bits; l sums the same rounded weights, so the
       // output stays an exact weighted average of the V rows
       if constexpr (MPV) p[r] = round16<KV>(p[r]);
       lsum[r] = lsum[r] * al[r] + p[r];
-      m[r] = mn;
+      m[r] = mn[r];
     }
     if ((lane >> 4) < QROWS) {
       const int hb = G > 4 ? 4 * (lane >> 4) : 0;
