@@ -220,34 +220,20 @@ __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
-// p rounded to the MFMA element type (kept in fp32), and two such values packed.
+// Matrix-core path: scores as K.Q^T, so that the MFMA's output layout (lane (n, kq): rows
+// 4kq + v, column n) gives each lane tokens 4kq .. 4kq+3 of head n % G, which is the A
+// operand layout P takes in P.V. One 16-byte K chunk (A) against the matching q piece(s)
+// (B): acc += A(k) * B(q).
 template <int KV>
-__device__ __forceinline__ float round16(float x) {
-  if constexpr (KV == PA_F16) return (float)(_Float16)x;
-  else return __uint_as_float((uint32_t)f32_to_bf16_rne(x) << 16);
-}
-template <int KV>
-__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
-  if constexpr (KV == PA_F16) {
-    const uint32_t l = __builtin_bit_cast(uint16_t, (_Float16)lo);
-    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)hi);
-    return l | h << 16;
-  } else {
-    // exact: both values were rounded to bf16 already
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-  }
-}
-
-// One 16-byte K chunk against the matching q piece(s): acc += A(q) * B(k).
-template <int KV>
-__device__ __forceinline__ f32x4 qk_chunk(f32x4 acc, u32x4 k, const u32x4* qc) {
+__device__ __forceinline__ f32x4 kq_chunk(f32x4 acc, u32x4 k, const u32x4* qc) {
   if constexpr (KV == PA_BF16) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qc[0]),
-                                                  __builtin_bit_cast(bf16x8, k), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                  __builtin_bit_cast(bf16x8, qc[0]), acc, 0, 0, 0);
   } else if constexpr (KV == PA_F16) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, qc[0]),
-                                                 __builtin_bit_cast(f16x8, k), acc, 0, 0, 0);
-  } else if constexpr (KV == PA_FP8_E4M3) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                 __builtin_bit_cast(f16x8, qc[0]), acc, 0, 0, 0);
+  } else {
+    static_assert(KV == PA_FP8_E4M3, "16-bit and fp8 K only");
     // 16 E4M3 values -> two groups of 8 bf16 (exact: every E4M3 value is a bf16 value)
     bf16x2 e[8];
 #pragma unroll
@@ -257,50 +243,74 @@ __device__ __forceinline__ f32x4 qk_chunk(f32x4 acc, u32x4 k, const u32x4* qc) {
     }
     bf16x8 k0 = {e[0][0], e[0][1], e[1][0], e[1][1], e[2][0], e[2][1], e[3][0], e[3][1]};
     bf16x8 k1 = {e[4][0], e[4][1], e[5][0], e[5][1], e[6][0], e[6][1], e[7][0], e[7][1]};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qc[0]), k0, acc,
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, __builtin_bit_cast(bf16x8, qc[0]), acc,
                                                   0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qc[1]), k1, acc,
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8, qc[1]), acc,
                                                   0, 0, 0);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(qc[0][e]), __uint_as_float(k[e]),
-                                                 acc, 0, 0, 0);
   }
   return acc;
 }
-
-// One V chunk (8 bytes of fp8, else 16 bytes) -> fp32 values.
-__device__ __forceinline__ void v_chunk_fp8(u32x2 w, float* v) {
+// p of four tokens rounded to the P.V element type (fp16 for fp16 K/V, else bf16, round to
+// nearest even) and packed as the MFMA A operand; pr gets the rounded values as fp32.
+template <int KV>
+__device__ __forceinline__ u32x2 round_pack4(const float (&p)[4], float (&pr)[4]) {
+  if constexpr (KV == PA_F16) {
+    _Float16 h[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-    v[4 * i] = lo[0];
-    v[4 * i + 1] = lo[1];
-    v[4 * i + 2] = hi[0];
-    v[4 * i + 3] = hi[1];
+    for (int v = 0; v < 4; ++v) {
+      h[v] = (_Float16)p[v];
+      pr[v] = (float)h[v];
+    }
+    return u32x2{(uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+                     (uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16,
+                 (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+                     (uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16};
+  } else {
+    const bf16x2 lo = {(__bf16)p[0], (__bf16)p[1]}, hi = {(__bf16)p[2], (__bf16)p[3]};
+    const u32x2 a = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    pr[0] = __uint_as_float(a[0] << 16);
+    pr[1] = __uint_as_float(a[0] & 0xffff0000u);
+    pr[2] = __uint_as_float(a[1] << 16);
+    pr[3] = __uint_as_float(a[1] & 0xffff0000u);
+    return a;
   }
 }
-template <int KV>
-__device__ __forceinline__ void v_chunk(u32x4 w, float* v) {
-  if constexpr (KV == PA_BF16) {
+// Max and sum over the four row groups of a column: lanes l, l ^ 16, l ^ 32, l ^ 48.
+// v_permlane16_swap / v_permlane32_swap exchange rows 0<->1, 2<->3 and the two halves,
+// so with both operands equal, the pair returned holds each lane's value and its
+// partner's, in some order.
+__device__ __forceinline__ float xrow_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  x = a > b ? a : b;
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  const float c = __uint_as_float(r2[0]), d = __uint_as_float(r2[1]);
+  return c > d ? c : d;
+}
+__device__ __forceinline__ float xrow_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+// DPP quad broadcast: every lane gets the value of lane I of its quad
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp<I * 0x55>(x);
+}
+
+// Vector-ALU path (fp32 K/V): one 16-byte K chunk against the matching q piece:
+// acc += A(q) * B(k), four 16x16x4 fp32 MFMAs.
+__device__ __forceinline__ f32x4 qk_chunk_f32(f32x4 acc, u32x4 k, const u32x4* qc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  } else if constexpr (KV == PA_F16) {
-    // Cast the whole 16-byte vector: hipcc 7.2 miscompiles a bit_cast of one u32 element
-    // to a 2 x half vector inside an unrolled loop (it reuses element 0 for every i).
-    const f16x8 h = __builtin_bit_cast(f16x8, w);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
-  } else {
-    static_assert(KV == PA_F32, "fp8 V chunks are 8 bytes (v_chunk_fp8)");
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
-  }
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(qc[0][e]), __uint_as_float(k[e]),
+                                               acc, 0, 0, 0);
+  return acc;
 }
 
 // Context length clamped to [0, cap]; cap = min(table width * 16, max_context_len).
@@ -376,7 +386,11 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   constexpr int NBUF_FIT = (256 - FIXED_VGPRS) / SLOT_VGPRS - 1;
   constexpr int NBUF_BYTES = kRingBytes / BLK_WAVE_BYTES;
   constexpr int NBUF_MIN = NBUF_BYTES < NBUF_FIT ? NBUF_BYTES : NBUF_FIT;
+#ifdef PA_NBUF
+  constexpr int NBUF = PA_NBUF;
+#else
   constexpr int NBUF = NBUF_MIN < 1 ? 1 : (NBUF_MIN > 3 ? 3 : NBUF_MIN);
+#endif
   constexpr int PBUF = kBlockTokens * G + 8;    // p of one block (+ alpha[8]), one wave
 
   __shared__ int s_lens[kMaxBatch];        // clamped context length per sequence
@@ -562,7 +576,8 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     const bool valid = (m.flags() & kValid) && (unsigned)pid < (unsigned)a.num_blocks;
     const int g = m.hg() * NW + wave;
     const size_t base = valid ? (size_t)pid * blk_stride + (size_t)g * ROWB : 0;
-    const uint32_t bytes = valid ? blk_stride - (uint32_t)g * ROWB : 0u;
+    // rows at or past L (the block's last rem tokens are valid) read as zero, unfetched
+    const uint32_t bytes = valid ? (uint32_t)(m.rem() - 1) * tok_stride + ROWB : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, bytes);
     const bool wantq = (m.flags() & (kValid | kFirst)) == (kValid | kFirst);
@@ -578,8 +593,9 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 
   // ---- 4. running state of the current piece
   u32x4 qreg[NL][QCH];
-  float m[HPL], lsum[HPL];
+  float m[HPL], lsum[HPL];                 // vector-ALU path: per head of the lane's rows
   float acc[G][VEPC];                      // vector-ALU P.V: lane (r, c), all G heads
+  float m1 = 0.0f, l1 = 0.0f;              // matrix-core path: head n % G, partial l
   f32x4 acc4[DPL];                         // matrix-core P.V: dim DPL*n + e, rows 4kq + v
   bool piece_whole_start = false;          // the current piece began at its segment's start
   int piece_slot = 0;
@@ -592,16 +608,18 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     if (!(fl & kValid)) return;
     const int g = mu.hg() * NW + wave;
     if (fl & kFirst) {
-      // a new piece: fresh (m, l, acc), and this head's q rows into the MFMA A layout
-#pragma unroll
-      for (int r = 0; r < HPL; ++r) {
-        m[r] = neg_inf();
-        lsum[r] = 0.0f;
-      }
+      // a new piece: fresh (m, l, acc), and this head's q rows into the MFMA operand layout
       if constexpr (MPV) {
+        m1 = neg_inf();
+        l1 = 0.0f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc4[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       } else {
+#pragma unroll
+        for (int r = 0; r < HPL; ++r) {
+          m[r] = neg_inf();
+          lsum[r] = 0.0f;
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -625,36 +643,86 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     }
     const int rem = mu.rem();              // tokens of this block below L
     const bool ragged = rem < kBlockTokens;
-    // scores of token t = lane % 16 for the heads of MFMA rows 4*(lane/16) + r
-    f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MPV) {
+      // lane (n, kq): scores of tokens 4kq + v (v < 4) for head n % G
+      const int kq = lane >> 4;
+      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < NL; ++s) sc = qk_chunk<KV>(sc, kb[s], qreg[s]);
-    const bool tok_ok = (lane & 15) < rem;
-    // (tok_ok holds on every lane of a full block, so the masks need no branch)
-    float al[HPL], p[HPL], sv[HPL], mn[HPL];
+      for (int s = 0; s < NL; ++s) sc = kq_chunk<KV>(sc, kb[s], qreg[s]);
+      float sv[4];
 #pragma unroll
-    for (int r = 0; r < HPL; ++r) {
-      sv[r] = tok_ok ? sc[r] * a.qk_scale_log2 : neg_inf();
-      mn[r] = sv[r] > m[r] ? sv[r] : m[r];   // m is the same on all lanes of a row
-    }
-    row16_max_n<HPL>(mn);                  // new running maxima, one per head
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = sc[v] * a.qk_scale_log2;
+        if (ragged) sv[v] = 4 * kq + v < rem ? sv[v] : neg_inf();
+      }
+      // new running max of head n % G: over the lane's 4 tokens and the running max, then
+      // over the 4 row groups, which hold the block's other tokens
+      const float b01 = sv[0] > sv[1] ? sv[0] : sv[1], b23 = sv[2] > sv[3] ? sv[2] : sv[3];
+      const float bm = b01 > b23 ? b01 : b23;
+      const float mn = xrow_max(bm > m1 ? bm : m1);
+      const float al1 = mn == neg_inf() ? 1.0f : fast_exp2(m1 - mn);
+      float pf[4], pr[4];
 #pragma unroll
-    for (int r = 0; r < HPL; ++r) {
-      al[r] = mn[r] == neg_inf() ? 1.0f : fast_exp2(m[r] - mn[r]);
-      p[r] = tok_ok ? fast_exp2(sv[r] - mn[r]) : 0.0f;
-      // the matrix cores take p in 16 bits; l sums the same rounded weights, so the
-      // output stays an exact weighted average of the V rows
-      if constexpr (MPV) p[r] = round16<KV>(p[r]);
-      lsum[r] = lsum[r] * al[r] + p[r];
-      m[r] = mn[r];
-    }
-    if ((lane >> 4) < QROWS) {
-      const int hb = G > 4 ? 4 * (lane >> 4) : 0;
-      if constexpr (MPV) {
-        // head-major: P[h][t]
+      for (int v = 0; v < 4; ++v) pf[v] = fast_exp2(sv[v] - mn);   // 0 for masked tokens
+      // the matrix cores take p in 16 bits; l sums the same rounded weights, so the output
+      // stays an exact weighted average of the V rows
+      const u32x2 aop = round_pack4<KV>(pf, pr);
+      l1 = l1 * al1 + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m1 = mn;
+      // rescale: accumulator row 4kq + v belongs to head (4kq + v) % G, whose factor lives
+      // in the lanes of column n with n % G == that head
+      if (__builtin_amdgcn_ballot_w64(al1 != 1.0f) != 0) {
+        float alv[4];
+        if constexpr (G <= 4) {
+          alv[0] = quad_bcast<0>(al1);
+          alv[1] = quad_bcast<1 % G>(al1);
+          alv[2] = quad_bcast<2 % G>(al1);
+          alv[3] = quad_bcast<3 % G>(al1);
+        } else {
 #pragma unroll
-        for (int r = 0; r < HPL; ++r) P[(hb + r) * kBlockTokens + (lane & 15)] = p[r];
-      } else {
+          for (int v = 0; v < 4; ++v) alv[v] = __shfl(al1, (lane & 48) + 4 * (kq & 1) + v);
+        }
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc4[e][v] *= alv[v];
+      }
+      // B operands: token rows 4kq + i of this lane's dims (rows at or past L read as zero)
+      constexpr int WORDS = DPL / 2;
+      uint32_t vw[4][WORDS];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v_words16<KV, WORDS>(vb[i], vw[i]);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 bop = {__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
+                           __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel)};
+        acc4[e] = mfma16<KV>(aop, bop, acc4[e]);
+      }
+    } else {
+      // vector-ALU P.V (fp32 K/V). Scores of token t = lane % 16 for the heads of MFMA rows
+      // 4*(lane/16) + r.
+      f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < NL; ++s) sc = qk_chunk_f32(sc, kb[s], qreg[s]);
+      const bool tok_ok = (lane & 15) < rem;
+      // (tok_ok holds on every lane of a full block, so the masks need no branch)
+      float al[HPL], p[HPL], sv[HPL], mn[HPL];
+#pragma unroll
+      for (int r = 0; r < HPL; ++r) {
+        sv[r] = tok_ok ? sc[r] * a.qk_scale_log2 : neg_inf();
+        mn[r] = sv[r] > m[r] ? sv[r] : m[r];   // m is the same on all lanes of a row
+      }
+      row16_max_n<HPL>(mn);                  // new running maxima, one per head
+#pragma unroll
+      for (int r = 0; r < HPL; ++r) {
+        al[r] = mn[r] == neg_inf() ? 1.0f : fast_exp2(m[r] - mn[r]);
+        p[r] = tok_ok ? fast_exp2(sv[r] - mn[r]) : 0.0f;
+        lsum[r] = lsum[r] * al[r] + p[r];
+        m[r] = mn[r];
+      }
+      if ((lane >> 4) < QROWS) {
+        const int hb = G > 4 ? 4 * (lane >> 4) : 0;
         float* dst = P + (lane & 15) * G + hb;
 #pragma unroll
         for (int r = 0; r < HPL; ++r) dst[r] = p[r];
@@ -664,97 +732,59 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
             for (int r = 0; r < HPL; ++r) P[kBlockTokens * G + hb + r] = al[r];
         }
       }
-    }
-    wave_lds_sync();
-
-    if constexpr (MPV) {
-      // rescale: accumulator rows 4kq + v belong to head (4kq + v) % G, whose factor this
-      // lane computed as al[v % HPL] (same row group in the QK^T and P.V layouts)
+      wave_lds_sync();
+      float alpha[G];
+      if constexpr (G > 4) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) alpha[h] = P[kBlockTokens * G + h];
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) alpha[h] = al[h];
+      }
       bool moved = false;
 #pragma unroll
-      for (int r = 0; r < HPL; ++r) moved |= al[r] != 1.0f;
+      for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.0f;
       if (moved) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc4[e][v] *= al[v % HPL];
+          for (int e = 0; e < VEPC; ++e) acc[h][e] *= alpha[h];
       }
-      // A operand: p of tokens 4kq .. 4kq+3 for head (lane % 16) % G
-      const f32x4 pp =
-          *reinterpret_cast<const f32x4*>(P + ((lane & 15) % G) * kBlockTokens + 4 * (lane >> 4));
-      const u32x2 aop = {pack16<KV>(pp[0], pp[1]), pack16<KV>(pp[2], pp[3])};
-      // B operands: token rows 4kq + i of this lane's dims; rows at or past L are zeroed
-      // (their p is 0, but the slot may hold NaN)
-      constexpr int WORDS = DPL / 2;
-      uint32_t vw[4][WORDS];
+      // V rows at or past L read as zero
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v_words16<KV, WORDS>(vb[i], vw[i]);
-        if (ragged) {
-          const bool ok = 4 * (lane >> 4) + i < rem;
+      for (int i = 0; i < NLV; ++i) {
+        const int row = lane / LPR + RPI * i;
+        float pv[G];
 #pragma unroll
-          for (int w = 0; w < WORDS; ++w) vw[i][w] = ok ? vw[i][w] : 0u;
-        }
+        for (int h = 0; h < G; ++h) pv[h] = P[row * G + h];
+        float v[VEPC];
+#pragma unroll
+        for (int e = 0; e < VEPC; ++e) v[e] = __uint_as_float(vb[i][e]);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < VEPC; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
       }
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 bop = {__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
-                           __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel)};
-        acc4[e] = mfma16<KV>(aop, bop, acc4[e]);
-      }
-    } else {
-
-    float alpha[G];
-    if constexpr (G > 4) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) alpha[h] = P[kBlockTokens * G + h];
-    } else {
-#pragma unroll
-      for (int h = 0; h < G; ++h) alpha[h] = al[h];
     }
-    bool moved = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.0f;
-    if (moved) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < VEPC; ++e) acc[h][e] *= alpha[h];
-    }
-#pragma unroll
-    for (int i = 0; i < NLV; ++i) {
-      const int row = lane / LPR + RPI * i;
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = P[row * G + h];
-      float v[VEPC];
-      if constexpr (KV == PA_FP8_E4M3) v_chunk_fp8(vb[i], v);
-      else v_chunk<KV>(vb[i], v);
-      if (ragged) {
-        const bool ok = row < rem;
-#pragma unroll
-        for (int e = 0; e < VEPC; ++e) v[e] = ok ? v[e] : 0.0f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < VEPC; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
-    }
-    }   // vector-ALU P.V
 
     if (!(fl & kLast)) return;
     // ---- the piece ends here: reduce over lanes, then write the output (whole segment)
     // or a record (a piece of a segment cut by a chunk boundary)
-#pragma unroll
-    for (int r = 0; r < HPL; ++r) lsum[r] = row16_sum(lsum[r]);
     const bool whole = piece_whole_start && (fl & kSegEnd);
     const size_t rec = ((size_t)mu.chunk() * 2 + piece_slot) * NW + wave;
     if constexpr (MPV) {
-      // every row group holds the full sums; lanes of row group kq < QROWS write heads
-      // hb + v (v < HPL) for dims DPL*n + e, with their own m and l
+      // l of head n % G over the whole block (the row groups held partial sums); lanes of
+      // row group kq < QROWS write heads hb + v (v < HPL) for dims DPL*n + e, taking m and
+      // l of head h from lane h
+      const float lt = xrow_sum(l1);
+      float m[HPL], lsum[HPL];
+      const int hb = G > 4 ? 4 * (lane >> 4) : 0;
+#pragma unroll
+      for (int v = 0; v < HPL; ++v) {
+        m[v] = __shfl(m1, (hb + v) & 15);
+        lsum[v] = __shfl(lt, (hb + v) & 15);
+      }
       if ((lane >> 4) < QROWS) {
-        const int hb = G > 4 ? 4 * (lane >> 4) : 0;
         const int n = lane & 15;
 #pragma unroll
         for (int v = 0; v < HPL; ++v) {
@@ -776,6 +806,8 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
         }
       }
     } else {
+#pragma unroll
+      for (int r = 0; r < HPL; ++r) lsum[r] = row16_sum(lsum[r]);
 #pragma unroll
       for (int st = LPR; st < kWave; st <<= 1)
 #pragma unroll
