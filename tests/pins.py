@@ -373,4 +373,86 @@ def pin_cow_isolation():
     assert (counts == S).sum() == nfull * w.notes["prompts"]
 
 
+# ---- fp8 E4M3 quantisation on the slot write (oracle.quantize) ----------------------
+
+def _e4m3_finite_codes():
+    t = oracle.e4m3_table()
+    return np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+
+
+def pin_e4m3_round_trip():
+    """Every finite code point encodes back to itself (254 of them: 0x7F, 0xFF are NaN)."""
+    import oracle.quantize as qz
+    codes = _e4m3_finite_codes()
+    assert len(codes) == 254
+    assert np.array_equal(qz.e4m3_encode(oracle.e4m3_table()[codes]), codes)
+
+
+def pin_e4m3_midpoints_to_even():
+    """Round to nearest, ties to the even mantissa, at every midpoint of both signs."""
+    import oracle.quantize as qz
+    t = oracle.e4m3_table()
+    for sign in (0x00, 0x80):
+        for c in range(0x7E):
+            lo, hi = t[sign | c], t[sign | (c + 1)]
+            mid = (lo + hi) / 2
+            even = c if c % 2 == 0 else c + 1
+            got = qz.e4m3_encode(np.array([mid - (hi - lo) / 16, mid, mid + (hi - lo) / 16]))
+            assert got.tolist() == [sign | c, sign | even, sign | (c + 1)], (hex(sign | c), mid)
+
+
+def pin_e4m3_saturation_nan_zero():
+    """Saturation to +-448 (infinities included), NaN -> 0x7F, signed zeros kept."""
+    import oracle.quantize as qz
+    y = np.array([448.0, 463.9, 464.0, 1e30, np.inf, -1000.0, -np.inf, np.nan, 0.0, -0.0,
+                  2.0 ** -10, 2.0 ** -10 * 1.001, -(2.0 ** -11)])
+    want = [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x00, 0x80, 0x00, 0x01, 0x80]
+    assert qz.e4m3_encode(y).tolist() == want
+
+
+def pin_e4m3_vs_torch_cast():
+    """torch's float8_e4m3fn cast (the same format, a library routine) on in-range values."""
+    import torch
+    import oracle.quantize as qz
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.normal(0, 1, 8000), rng.normal(0, 60, 8000),
+                        rng.uniform(-447.0, 447.0, 8000), rng.normal(0, 0.01, 8000)])
+    y = y.astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(qz.e4m3_encode(y), ref)
+
+
+def pin_quant_power_of_two_scale():
+    """With a power-of-two scale s, x = v * s for every E4M3 value v encodes to v's code
+    (the scale divides, exactly), from fp32, fp16 and bf16 sources."""
+    import oracle.quantize as qz
+    t = oracle.e4m3_table()
+    codes = np.array([c for c in _e4m3_finite_codes() if abs(t[c]) >= 2.0 ** -6], dtype=np.uint8)
+    x = t[codes] * 8.0
+    for kind, store in (("f32", x.astype(np.float32)), ("f16", x.astype(np.float16)),
+                        ("bf16", (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))):
+        y = qz.quant_inputs(store, kind, 8.0)
+        assert y.dtype == np.float32
+        assert np.array_equal(qz.e4m3_encode(y), codes), kind
+
+
+def pin_cache_write_fp8_closed_form():
+    """Slot s receives the codes of its new row (block s // 16, row s % 16); -1 skips;
+    decoding the codes gives new / scale to within half a code spacing."""
+    import oracle.quantize as qz
+    rng = np.random.default_rng(1)
+    pool = rng.integers(0, 256, size=(4, 16, 2, 8), dtype=np.uint8)
+    new = rng.normal(0, 3, size=(3, 2, 8)).astype(np.float32)
+    out = qz.cache_write_fp8_ref(pool, new, "f32", 0.5, np.array([5, -1, 63]))
+    touched = np.zeros(out.shape[:2], dtype=bool)
+    touched[0, 5] = touched[3, 15] = True
+    assert np.array_equal(out[~touched], pool[~touched])
+    for (blk, row), t in (((0, 5), 0), ((3, 15), 2)):
+        dec = oracle.decode_storage(out[blk, row], "fp8_e4m3")
+        target = np.clip(new[t].astype(np.float64) / 0.5, -448, 448)
+        spacing = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(target), 2.0 ** -6))) - 3),
+                             2.0 ** -9)
+        assert np.all(np.abs(dec - target) <= spacing / 2 + 1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -10,6 +10,7 @@ import pytest
 import oracle
 import oracle.attention as att
 import oracle.cache_ops as cops
+import oracle.quantize as qz
 import oracle.storage as st
 from pins import ALL_PINS
 
@@ -89,6 +90,36 @@ def _copy_reversed(pool, pairs):
     return out
 
 
+_good_encode = qz.e4m3_encode
+
+
+def _encode_ties_away(y):
+    out = _good_encode(y)
+    y = np.asarray(y, dtype=np.float64).reshape(-1)
+    flat = out.reshape(-1).copy()
+    t = oracle.e4m3_table()
+    for i, v in enumerate(y):               # at a tie take the larger magnitude instead
+        c = int(flat[i]) & 0x7F
+        if 0 < c < 0x7E and not np.isnan(v) and abs(v) == (t[c] + t[c + 1]) / 2:
+            flat[i] = (int(flat[i]) & 0x80) | (c + 1)
+    return flat.reshape(out.shape)
+
+
+def _encode_no_saturation(y):
+    out = _good_encode(y)
+    big = np.abs(np.asarray(y, dtype=np.float64)) > 448.0
+    return np.where(big, np.uint8(0x7F), out).astype(np.uint8)
+
+
+def _encode_sign_dropped(y):
+    return _good_encode(np.abs(np.asarray(y, dtype=np.float64)))
+
+
+def _quant_scale_multiplies(new, kind, scale):
+    x = st.decode_storage(new, kind).astype(np.float32)
+    return x * np.float32(scale)
+
+
 MUTATIONS = {
     "gqa_interleaved": (att, "kv_head_of", _interleaved_gqa),
     "no_length_mask": (att, "gather_sequence", _no_truncation),
@@ -100,6 +131,10 @@ MUTATIONS = {
     "bf16_low_half": (st, "bf16_bits_to_f64", _bf16_low_half),
     "slot_index_swapped": (cops, "cache_write_ref", _write_swapped),
     "copy_direction_reversed": (cops, "block_copy_ref", _copy_reversed),
+    "e4m3_ties_away_from_zero": (qz, "e4m3_encode", _encode_ties_away),
+    "e4m3_no_saturation": (qz, "e4m3_encode", _encode_no_saturation),
+    "e4m3_sign_dropped": (qz, "e4m3_encode", _encode_sign_dropped),
+    "quant_scale_multiplies": (qz, "quant_inputs", _quant_scale_multiplies),
 }
 
 
