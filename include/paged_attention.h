@@ -153,6 +153,27 @@ pa_status_t pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const 
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, int32_t kv_dtype, void* stream);
 
+/* Slot write into an fp8 E4M3 cache, quantising the new values (setting the KV cache to
+ * fp8 E4M3 halves its memory: vLLM-PagedAttention与连续批处理技术拆解, section 五, the
+ * flag table and the KV cache quantisation note). For each t < num_tokens with
+ * slot_mapping[t] = s >= 0 and every element x of k_new[t] (of v_new[t] with v_scale):
+ *   y = fp32(x) * fp32(1 / k_scale)          one binary32 multiply, round to nearest even
+ *   k_pool byte = E4M3FN(y)                  nearest value, ties to the even mantissa;
+ *                                            |y| >= 448 (and +-inf) saturate to +-448;
+ *                                            NaN -> 0x7F; the sign of zero is kept
+ * so that decoding code * k_scale (pa_decode's k_scale) approximates x. Pools are OCP
+ * E4M3FN bytes [N, block_size, Hkv, d]; k_new, v_new [T, Hkv, d] in src_dtype (PA_F32,
+ * PA_F16 or PA_BF16; PA_FP8_E4M3 sources use pa_cache_write); slot_mapping [T] int64,
+ * as for pa_cache_write (s < 0 skips, out-of-range slots are skipped). k_scale and
+ * v_scale must be finite and > 0 (else PA_ERR_SHAPE); Hkv * d must be a multiple of 16.
+ * fp32 subnormal inputs may be flushed to zero of either sign by the hardware conversion
+ * (they lie far below E4M3's smallest value, 2^-9, and encode as zero). */
+pa_status_t pa_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t src_dtype, float k_scale,
+                               float v_scale, void* stream);
+
 /* Copy-on-write block copy: a shared block is read-only and a sequence that must write
  * into it copies it first (vLLM-PagedAttention与连续批处理技术拆解, section 3.4). For
  * each pair p: k_pool[dst_p] = k_pool[src_p] and v_pool[dst_p] = v_pool[src_p], whole

@@ -8,5 +8,5 @@ library is not built the calls raise; there is no fallback path.
 from .binding import (  # noqa: F401
     PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PaError, DecodeDesc, lib_path, load_library,
     pa_abi_version, pa_status_string, pa_decode_max_chunks, decode_workspace, pa_decode_workspace_bytes,
-    pa_decode, pa_cache_write, pa_block_copy,
+    pa_decode, pa_cache_write, pa_cache_write_fp8, pa_block_copy,
 )

@@ -56,6 +56,8 @@ def load_library():
     lib.pa_decode.argtypes = [D, P, P, P, P, P, P, I32, F, F, F, P, SZ, P]
     lib.pa_cache_write.restype = I32
     lib.pa_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P]
+    lib.pa_cache_write_fp8.restype = I32
+    lib.pa_cache_write_fp8.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, F, P]
     lib.pa_block_copy.restype = I32
     lib.pa_block_copy.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P]
     _LIB = lib
@@ -174,6 +176,31 @@ def pa_cache_write(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
                             T, Hkv, d, bs, N, dtype_code(k_pool), _stream(stream))
     if st != 0:
         raise PaError(st, "pa_cache_write")
+
+
+def pa_cache_write_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale=1.0, v_scale=1.0,
+                       stream=None):
+    """Write new tokens' K/V [T, Hkv, d] (float32, float16 or bfloat16) into the slots of
+    fp8 E4M3 pools (uint8 or float8_e4m3fn), quantising with per-tensor dequantisation
+    scales k_scale, v_scale."""
+    import torch
+    lib = load_library()
+    N, bs, Hkv, d = k_pool.shape
+    T = slot_mapping.shape[0]
+    if k_new.shape != (T, Hkv, d) or v_new.shape != (T, Hkv, d):
+        raise ValueError("k_new / v_new must be [num_tokens, num_kv_heads, head_dim]")
+    if v_pool.shape != k_pool.shape or dtype_code(k_pool) != PA_FP8_E4M3 or \
+            dtype_code(v_pool) != PA_FP8_E4M3:
+        raise ValueError("pools must be fp8 E4M3 bytes of the same shape")
+    if v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    st = lib.pa_cache_write_fp8(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                _dev(slot_mapping, "slot_mapping", torch.int64), T, Hkv, d, bs,
+                                N, dtype_code(k_new), float(k_scale), float(v_scale),
+                                _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_cache_write_fp8")
 
 
 def pa_block_copy(k_pool, v_pool, src_dst_pairs, stream=None):

@@ -238,6 +238,35 @@ pa_status_t pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const 
   return PA_OK;
 }
 
+pa_status_t pa_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t src_dtype, float k_scale,
+                               float v_scale, void* stream) {
+  int64_t row_bytes = 0;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  pa_status_t st = check_cache_args(num_kv_heads, head_dim, block_size, num_blocks,
+                                    PA_FP8_E4M3, &row_bytes);
+  if (st != PA_OK) return st;
+  if (!valid_dtype(src_dtype)) return PA_ERR_DTYPE;
+  if (src_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;   // use pa_cache_write
+  if (!(isfinite(k_scale) && k_scale > 0.0f && isfinite(v_scale) && v_scale > 0.0f))
+    return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_ALIGN;
+  // one binary32 reciprocal of each scale, rounded to nearest
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (pa::launch_cache_write_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                                 (int32_t)row_bytes, num_slots, src_dtype, k_inv, v_inv,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
 pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int32_t num_blocks, int32_t kv_dtype,

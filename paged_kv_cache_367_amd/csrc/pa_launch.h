@@ -111,6 +111,11 @@ hipError_t launch_merge(int out_dtype, int head_dim, int group, const MergeArgs&
 hipError_t launch_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                               const int64_t* slot_mapping, int32_t num_tokens,
                               int32_t row_bytes, int64_t num_slots, hipStream_t stream);
+hipError_t launch_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new,
+                                  const void* v_new, const int64_t* slot_mapping,
+                                  int32_t num_tokens, int32_t row_elems, int64_t num_slots,
+                                  int32_t src_dtype, float k_inv, float v_inv,
+                                  hipStream_t stream);
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int64_t* pairs,
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream);

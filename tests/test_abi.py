@@ -122,6 +122,18 @@ def test_cache_ops_reject_before_launch(lib):
     assert lib.pa_cache_write(p, p, p, p, p, 4, 1, 3, 16, 100, pa.PA_FP8_E4M3, None) == -4
     assert lib.pa_cache_write(p, p, ctypes.c_void_p(0x10004), p, p, 4, 8, 128, 16, 100,
                               pa.PA_BF16, None) == -6
+    f = ctypes.c_float
+    q8 = lambda *a: lib.pa_cache_write_fp8(*a)                     # noqa: E731
+    assert q8(p, p, p, p, p, -1, 8, 128, 16, 100, pa.PA_BF16, f(1), f(1), None) == -2
+    assert q8(p, p, p, p, p, 0, 8, 128, 16, 100, pa.PA_F32, f(1), f(1), None) == 0
+    assert q8(z, p, p, p, p, 4, 8, 128, 16, 100, pa.PA_F16, f(1), f(1), None) == -1
+    assert q8(p, p, p, p, p, 4, 8, 128, 16, 100, 9, f(1), f(1), None) == -3
+    assert q8(p, p, p, p, p, 4, 8, 128, 16, 100, pa.PA_FP8_E4M3, f(1), f(1), None) == -4
+    assert q8(p, p, p, p, p, 4, 1, 8, 16, 100, pa.PA_F32, f(1), f(1), None) == -4   # row of 8 B
+    assert q8(p, p, p, p, p, 4, 8, 128, 16, 100, pa.PA_F32, f(0), f(1), None) == -2
+    assert q8(p, p, p, p, p, 4, 8, 128, 16, 100, pa.PA_F32, f(1), f(float("inf")), None) == -2
+    assert q8(p, p, ctypes.c_void_p(0x10008), p, p, 4, 8, 128, 16, 100, pa.PA_F32, f(1), f(1),
+              None) == -6
     assert lib.pa_block_copy(p, p, p, -1, 8, 128, 16, 100, pa.PA_BF16, None) == -2
     assert lib.pa_block_copy(p, p, z, 3, 8, 128, 16, 100, pa.PA_BF16, None) == -1
     assert lib.pa_block_copy(p, p, p, 0, 8, 128, 16, 100, pa.PA_BF16, None) == 0

@@ -60,6 +60,87 @@ def test_cache_write_fp8_bits():
     assert np.array_equal(d["v"].cpu().numpy(), oracle.cache_write_ref(w.v_pool, v_new, slots))
 
 
+def _quant_case(kind, T, Hkv, d, scale, seed):
+    """New rows spanning the E4M3 range at this scale, with ties (code midpoints),
+    saturation, infinities, NaN and signed zeros; returns (storage array, torch tensor)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 1, (T, Hkv, d)) * rng.choice([0.003, 0.1, 1.0, 30.0, 300.0, 3000.0],
+                                                    size=(T, Hkv, 1))
+    t = oracle.e4m3_table()
+    mids = np.array([(t[c] + t[c + 1]) / 2 for c in range(0, 0x7E, 5)])
+    edge = np.concatenate([mids, -mids, [0.0, -0.0, np.inf, -np.inf, np.nan, 448.0, 449.0,
+                                         -460.0, 470.0, 2.0 ** -10, -(2.0 ** -11), 1e4]])
+    flat = x.reshape(-1)
+    flat[:edge.size] = edge * scale
+    x32 = x.astype(np.float32)
+    if kind == "f32":
+        return x32, torch.from_numpy(x32).cuda()
+    if kind == "f16":
+        x16 = x32.astype(np.float16)
+        return x16, torch.from_numpy(x16).cuda()
+    bits = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bits, torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.5, 0.0371])
+def test_cache_write_fp8_quantises_bit_exact(kind, scale):
+    import torch
+    rng = np.random.default_rng(11)
+    N, Hkv, d, T = 40, 8, 128, 200
+    k_pool = rng.integers(0, 256, size=(N, 16, Hkv, d), dtype=np.uint8)
+    v_pool = rng.integers(0, 256, size=(N, 16, Hkv, d), dtype=np.uint8)
+    slots = rng.choice(N * 16, size=T, replace=False).astype(np.int64)
+    slots[3] = -1                                  # skipped
+    slots[7] = N * 16 + 5                          # outside the pool: skipped
+    k_store, k_dev = _quant_case(kind, T, Hkv, d, scale, 1)
+    v_store, v_dev = _quant_case(kind, T, Hkv, d, 2 * scale, 2)
+    kp, vp = torch.from_numpy(k_pool).cuda(), torch.from_numpy(v_pool).cuda()
+    pa.pa_cache_write_fp8(kp, vp, k_dev, v_dev, torch.from_numpy(slots).cuda(),
+                          k_scale=scale, v_scale=2 * scale)
+    _sync()
+    ref_slots = slots.copy()
+    ref_slots[7] = -1
+    k_ref = oracle.cache_write_fp8_ref(k_pool, k_store, kind, scale, ref_slots)
+    v_ref = oracle.cache_write_fp8_ref(v_pool, v_store, kind, 2 * scale, ref_slots)
+    k_got, v_got = kp.cpu().numpy(), vp.cpu().numpy()
+    bad = np.argwhere(k_got != k_ref)
+    assert bad.size == 0, f"{len(bad)} K bytes differ, first at {bad[:3].tolist()}: " \
+        f"gpu {k_got[tuple(bad[0])]:#04x} oracle {k_ref[tuple(bad[0])]:#04x}"
+    assert np.array_equal(v_got, v_ref)
+
+
+def test_cache_write_fp8_then_decode():
+    """Quantise the new tokens into an fp8 pool on the GPU, decode, compare with the
+    oracle's decode of the oracle-quantised pool (5e-2, the fp8 tolerance)."""
+    import torch
+    from gpu_harness import max_abs_err
+    w = wl.make(5, batch=3, len_range=(200, 700))
+    rng = np.random.default_rng(8)
+    B = w.batch
+    # one new token per sequence, in its tail slot (position L - 1)
+    slots = np.array([w.block_tables[b, (w.context_lens[b] - 1) // 16] * 16 +
+                      (w.context_lens[b] - 1) % 16 for b in range(B)], dtype=np.int64)
+    k_new = rng.normal(0, 1, (B, w.num_kv_heads, w.head_dim)).astype(np.float32)
+    v_new = rng.normal(0, 1, (B, w.num_kv_heads, w.head_dim)).astype(np.float32)
+    d = to_device(w)
+    pa.pa_cache_write_fp8(d["k"], d["v"], torch.from_numpy(k_new).cuda(),
+                          torch.from_numpy(v_new).cuda(), torch.from_numpy(slots).cuda(),
+                          k_scale=w.k_scale, v_scale=w.v_scale)
+    out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda")
+    pa.pa_decode(out, d["q"], d["k"], d["v"], d["tables"], d["lens"], w.max_context_len,
+                 w.scale, w.k_scale, w.v_scale)
+    _sync()
+    k_ref = oracle.cache_write_fp8_ref(w.k_pool, k_new, "f32", w.k_scale, slots)
+    v_ref = oracle.cache_write_fp8_ref(w.v_pool, v_new, "f32", w.v_scale, slots)
+    assert np.array_equal(d["k"].cpu().numpy(), k_ref)
+    ref = oracle.decode_ref(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale,
+                            q_kind=w.q_dtype, kv_kind="fp8_e4m3", k_scale=w.k_scale,
+                            v_scale=w.v_scale)
+    assert max_abs_err(out.float().cpu().numpy().astype(np.float64), ref) <= 5e-2
+
+
 @pytest.mark.parametrize("idx,kw", [(4, dict(batch=2)), (4, {})])
 def test_block_copy_bit_exact_and_cow_isolation(idx, kw):
     w = wl.make(idx, **kw)
