@@ -15,6 +15,8 @@ Everything is plain numpy in float64:
                softmax attention per query head (GQA kv head = h // group).
   cache_ops    cache_write_ref (slot write of new tokens) and block_copy_ref
                (copy-on-write block copy), both bit copies.
+  prefill      prefill_ref: n new query tokens per sequence attending causally over
+               the paged cache (chunked prefill, prefix-cache tail prefill).
   quantize     e4m3_encode and cache_write_fp8_ref: the slot write into an fp8 E4M3
                cache, quantising each new value by a per-tensor scale.
   formulas     the per-token KV size formula.
@@ -26,6 +28,7 @@ from .storage import decode_storage, e4m3_table, bf16_bits_to_f64
 from .attention import decode_ref, attend, gather_sequence, kv_head_of
 from .cache_ops import cache_write_ref, block_copy_ref
 from .quantize import e4m3_encode, quant_inputs, cache_write_fp8_ref
+from .prefill import prefill_ref, query_positions
 from .formulas import kv_bytes_per_token, kv_bytes_per_request
 
 __all__ = [
@@ -33,5 +36,6 @@ __all__ = [
     "decode_ref", "attend", "gather_sequence", "kv_head_of",
     "cache_write_ref", "block_copy_ref",
     "e4m3_encode", "quant_inputs", "cache_write_fp8_ref",
+    "prefill_ref", "query_positions",
     "kv_bytes_per_token", "kv_bytes_per_request",
 ]

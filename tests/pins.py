@@ -455,4 +455,103 @@ def pin_cache_write_fp8_closed_form():
         assert np.all(np.abs(dec - target) <= spacing / 2 + 1e-12)
 
 
+# ---- multi-token queries over the paged cache (oracle.prefill) ----------------------
+
+def _prefill_case(n_per_seq, kv="bf16", G=4, Hkv=2, d=64, seed=3):
+    """A small paged workload with n_per_seq[b] query tokens at the end of sequence b."""
+    rng = np.random.default_rng(seed)
+    w = wl.make(3, batch=len(n_per_seq), len_range=(20, 90), seed_offset=seed)
+    # the workload's lengths and block tables, with pools of Hkv heads of d dims
+    N = w.num_blocks
+    k = wl._normal_storage(rng, (N, 16, Hkv, d), kv)
+    v = wl._normal_storage(rng, (N, 16, Hkv, d), kv)
+    qs = np.concatenate([[0], np.cumsum(n_per_seq)]).astype(np.int64)
+    q = wl._normal_storage(rng, (int(qs[-1]), G * Hkv, d), "bf16")
+    return dict(q=q, qs=qs, k=k, v=v, tables=w.block_tables, lens=w.context_lens,
+                scale=1.0 / np.sqrt(d), kv=kv)
+
+
+def _prefill(c, **kw):
+    import oracle.prefill as pf
+    args = dict(c, **kw)
+    return pf.prefill_ref(args["q"], args["qs"], args["k"], args["v"], args["tables"],
+                          args["lens"], args["scale"], q_kind="bf16", kv_kind=args["kv"])
+
+
+def pin_prefill_one_token_is_decode():
+    """One query token per sequence is exactly a decode step (same bits)."""
+    c = _prefill_case([1, 1, 1, 1])
+    got = _prefill(c)
+    ref = oracle.decode_ref(c["q"], c["k"], c["v"], c["tables"], c["lens"], c["scale"],
+                            q_kind="bf16", kv_kind="bf16")
+    assert np.array_equal(got, ref)
+
+
+def pin_prefill_causality():
+    """A token never sees later positions: changing K and V at position p leaves every
+    query token before p unchanged (bitwise) and changes the tokens at or after it."""
+    c = _prefill_case([9, 3])
+    base = _prefill(c)
+    b, L, n = 0, int(c["lens"][0]), 9
+    p = L - 4                                       # among the query tokens: i = n - 4
+    k2, v2 = c["k"].copy(), c["v"].copy()
+    blk, row = c["tables"][b][p // 16], p % 16
+    k2[blk, row] = np.uint16(0x4040)                         # bf16 3.0: a large change
+    v2[blk, row] = np.uint16(0xC000)                         # bf16 -2.0
+    pert = _prefill(c, k=k2, v=v2)
+    i_p = p - (L - n)
+    assert np.array_equal(pert[:i_p], base[:i_p])
+    assert np.all(np.abs(pert[i_p:n] - base[i_p:n]).max(axis=(1, 2)) > 1e-6)
+    assert np.array_equal(pert[n:], base[n:])                  # the other sequence
+
+
+def pin_prefill_vs_sdpa():
+    """torch's scaled_dot_product_attention in float64 with an explicit end-aligned
+    causal mask on the contiguous K/V (a library routine with its own masking)."""
+    import torch
+    c = _prefill_case([6, 2, 11], G=2, Hkv=2)
+    got = _prefill(c)
+    G = c["q"].shape[1] // c["k"].shape[2]
+    for b in range(3):
+        L, n = int(c["lens"][b]), int(c["qs"][b + 1] - c["qs"][b])
+        K = oracle.decode_storage(oracle.gather_sequence(c["k"], c["tables"][b], L, 16,
+                                                         c["k"].shape[0]), "bf16")
+        V = oracle.decode_storage(oracle.gather_sequence(c["v"], c["tables"][b], L, 16,
+                                                         c["v"].shape[0]), "bf16")
+        Q = oracle.decode_storage(c["q"][c["qs"][b]:c["qs"][b + 1]], "bf16")
+        Kh = np.repeat(K, G, axis=1).transpose(1, 0, 2)[None]      # [1, Hq, L, d]
+        Vh = np.repeat(V, G, axis=1).transpose(1, 0, 2)[None]
+        Qh = Q.transpose(1, 0, 2)[None]                              # [1, Hq, n, d]
+        mask = np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Qh), torch.from_numpy(Kh), torch.from_numpy(Vh),
+            attn_mask=torch.from_numpy(mask), scale=c["scale"]).numpy()[0].transpose(1, 0, 2)
+        assert np.abs(got[c["qs"][b]:c["qs"][b + 1]] - ref).max() < 1e-12
+
+
+def pin_prefill_full_prompt_first_token():
+    """With every cached token a query token (n = L), token 0 attends to itself only,
+    so its output is its own V row exactly."""
+    c = _prefill_case([1])
+    L = int(c["lens"][0])
+    c["qs"] = np.array([0, L])
+    rng = np.random.default_rng(9)
+    c["q"] = wl._normal_storage(rng, (L, c["q"].shape[1], c["q"].shape[2]), "bf16")
+    got = _prefill(c)
+    V0 = oracle.decode_storage(c["v"][c["tables"][0][0], 0], "bf16")      # [Hkv, d]
+    G = c["q"].shape[1] // c["v"].shape[2]
+    assert np.array_equal(got[0], np.repeat(V0, G, axis=0))
+
+
+def pin_prefill_sequences_independent():
+    """Sequence b's outputs depend on its own query rows only."""
+    c = _prefill_case([4, 5, 2])
+    base = _prefill(c)
+    q2 = c["q"].copy()
+    q2[4:9] = q2[4:9] ^ np.uint16(0x0100)                       # sequence 1's rows
+    pert = _prefill(c, q=q2)
+    assert np.array_equal(pert[:4], base[:4]) and np.array_equal(pert[9:], base[9:])
+    assert not np.array_equal(pert[4:9], base[4:9])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

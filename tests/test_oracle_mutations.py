@@ -10,6 +10,7 @@ import pytest
 import oracle
 import oracle.attention as att
 import oracle.cache_ops as cops
+import oracle.prefill as pf
 import oracle.quantize as qz
 import oracle.storage as st
 from pins import ALL_PINS
@@ -120,6 +121,35 @@ def _quant_scale_multiplies(new, kind, scale):
     return x * np.float32(scale)
 
 
+def _positions_from_start(L, n):
+    return np.arange(0, n)                  # query token i at position i, not L - n + i
+
+
+_good_attend = att.attend
+
+
+def _prefill_no_causal_mask(q, query_start, k_pool, v_pool, block_tables, context_lens, scale,
+                            *, q_kind, kv_kind, k_scale=1.0, v_scale=1.0):
+    B = len(query_start) - 1
+    out = np.zeros(q.shape, dtype=np.float64)
+    G = q.shape[1] // k_pool.shape[2]
+    N, bs = k_pool.shape[:2]
+    for b in range(B):
+        L = int(context_lens[b])
+        K = st.decode_storage(att.gather_sequence(k_pool, block_tables[b], L, bs, N), kv_kind)
+        V = st.decode_storage(att.gather_sequence(v_pool, block_tables[b], L, bs, N), kv_kind)
+        for r in range(int(query_start[b]), int(query_start[b + 1])):
+            qv = st.decode_storage(q[r], q_kind)
+            for h in range(q.shape[1]):    # every token attends over all L positions
+                out[r, h], _ = _good_attend(qv[h], K[:, h // G] * k_scale, V[:, h // G] * v_scale,
+                                            scale)
+    return out
+
+
+def _positions_one_early(L, n):
+    return np.arange(L - n, L) - 1          # the mask stops one position short
+
+
 MUTATIONS = {
     "gqa_interleaved": (att, "kv_head_of", _interleaved_gqa),
     "no_length_mask": (att, "gather_sequence", _no_truncation),
@@ -135,6 +165,9 @@ MUTATIONS = {
     "e4m3_no_saturation": (qz, "e4m3_encode", _encode_no_saturation),
     "e4m3_sign_dropped": (qz, "e4m3_encode", _encode_sign_dropped),
     "quant_scale_multiplies": (qz, "quant_inputs", _quant_scale_multiplies),
+    "prefill_positions_from_start": (pf, "query_positions", _positions_from_start),
+    "prefill_no_causal_mask": (pf, "prefill_ref", _prefill_no_causal_mask),
+    "prefill_mask_one_short": (pf, "query_positions", _positions_one_early),
 }
 
 
