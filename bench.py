@@ -15,7 +15,13 @@ token each) per second for this one attention layer. `roofline` describes the de
 launch (main + merge kernels), timed with HIP events on the stream it runs on.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3]
+With --path prefill the step is one chunked-prefill step instead (workload.chunked_prefill:
+16 prompts x 512 new tokens over contexts of up to 8192): the slot write of the chunk's
+K/V, then causal multi-token attention (pa_prefill). Its value is attention TFLOP/s
+counting only the unmasked work, 4 * d * Hq flops per (query token, attended position),
+and its roofline is the bf16 matrix-core peak.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3] [--path decode|prefill]
 """
 from __future__ import annotations
 
@@ -33,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn decode KV-read GB/s (% HBM peak) & tokens/s, 8B GQA bf16 layer"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
+PREFILL_METRIC = "paged-attn chunked-prefill attention TFLOP/s (causal, algorithmic), 8B GQA bf16 layer"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_367_amd", "csrc", "pa_decode.hip")
 
@@ -92,6 +100,154 @@ def cpu_baseline(w, gpu_out, k_after, v_after, budget_s: float):
     }
 
 
+def prefill_flops(w) -> float:
+    """Unmasked attention work: 4 * d * Hq flops (2 for q.k, 2 for p.v) per query token
+    and attended position; token i of a sequence with L cached and n new tokens attends
+    over L - n + i + 1 positions."""
+    import numpy as np
+    L = w.context_lens.astype(np.int64)
+    n = w.query_lens
+    pairs = n * (L - n) + n * (n + 1) // 2
+    return float(4 * w.head_dim * w.num_q_heads * int(pairs.sum()))
+
+
+def prefill_cpu_baseline(w, gpu_out, budget_s: float):
+    """Time the oracle on query rows in a seeded order until ~budget_s of CPU work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:  # noqa: BLE001 - reporting only
+        threads = None
+    order = np.random.default_rng(0).permutation(w.num_query_tokens)
+    seq_of = np.searchsorted(w.query_start, np.arange(w.num_query_tokens), side="right") - 1
+    done, flops, err = [], 0.0, 0.0
+    t0 = time.perf_counter()
+    for r in order:
+        ref = oracle.prefill_ref(w.q, w.query_start, w.k_pool, w.v_pool, w.block_tables,
+                                 w.context_lens, w.scale, q_kind=w.q_dtype, kv_kind=w.kv_dtype,
+                                 k_scale=w.k_scale, v_scale=w.v_scale, rows=[int(r)])
+        b = int(seq_of[r])
+        pos = int(w.context_lens[b]) - int(w.query_lens[b]) + int(r - w.query_start[b])
+        flops += 4.0 * w.head_dim * w.num_q_heads * (pos + 1)
+        err = max(err, float(np.max(np.abs(gpu_out[r] - ref[r]))))
+        done.append(int(r))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+        "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": f"{len(done)} of {w.num_query_tokens} query rows (all {w.num_q_heads} heads), "
+                  f"fp64 numpy, {dt:.1f} s",
+        "sample_max_abs_err_vs_gpu": err,
+    }
+
+
+def run_prefill(args) -> int:
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_367_amd as pa
+    import workload as wl
+
+    log("building the chunked-prefill workload")
+    t0 = time.perf_counter()
+    w = wl.chunked_prefill()
+    B = w.batch
+    log(f"workload {w.name}: B={B} query tokens={w.num_query_tokens} "
+        f"context tokens={int(w.context_lens.sum())} pool_blocks={w.num_blocks} "
+        f"({time.perf_counter() - t0:.1f} s)")
+    # the chunk's own K/V rows, written to their slots at the start of every step (the
+    # values already there, so every step computes the same thing)
+    L = w.context_lens.astype(np.int64)
+    tok_seq = np.repeat(np.arange(B), w.query_lens)
+    pos = L[tok_seq] - w.query_lens[tok_seq] + (np.arange(w.num_query_tokens) -
+                                                w.query_start[tok_seq])
+    slots = w.block_tables[tok_seq, pos // 16].astype(np.int64) * 16 + pos % 16
+    k_new = w.k_pool.reshape(-1, w.num_kv_heads, w.head_dim)[slots]
+    v_new = w.v_pool.reshape(-1, w.num_kv_heads, w.head_dim)[slots]
+
+    def dev(a, kind=None):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if kind == "bf16" \
+            else torch.from_numpy(a)
+        return t.cuda()
+
+    q = dev(w.q, w.q_dtype)
+    tables, lens, qs = dev(w.block_tables), dev(w.context_lens), dev(w.query_start)
+    R = max(1, args.replicas)
+    ks = [dev(w.k_pool, w.kv_dtype) for _ in range(R)]
+    vs = [dev(w.v_pool, w.kv_dtype) for _ in range(R)]
+    d_slots = dev(slots)
+    d_knew, d_vnew = dev(k_new, w.kv_dtype), dev(v_new, w.kv_dtype)
+    out = torch.empty(tuple(w.q.shape), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"resident: {R} pool replicas")
+    flops = prefill_flops(w)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i, timed):
+        r = i % R
+        pa.pa_cache_write(ks[r], vs[r], d_knew, d_vnew, d_slots)
+        if timed:
+            ev0[i].record()
+        pa.pa_prefill(out, q, ks[r], vs[r], tables, lens, qs, w.max_query_len, w.scale,
+                      w.k_scale, w.v_scale)
+        if timed:
+            ev1[i].record()
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    lms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    lavg = sum(lms) / len(lms)
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step, prefill launch avg {lavg:.4f} ms "
+        f"(min {min(lms):.4f}, max {max(lms):.4f})")
+    achieved = flops / (lavg * 1e-3) / 1e12
+    record = {
+        "metric": PREFILL_METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded, workload.py)",
+        "config": {
+            "workload": w.name, "batch": B, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+            "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "accumulate": "f32",
+            "query_tokens": w.num_query_tokens, "context_tokens": int(L.sum()),
+            "max_query_len": w.max_query_len, "flops_per_step": flops, "pool_replicas": R,
+            "seed": w.seed,
+        },
+        "query_tokens_per_s": w.num_query_tokens / (ms * 1e-3),
+        "roofline": {
+            "kernel": "pa_prefill (prefill_kernel)", "bound": "mfma", "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "launch_ms": lavg,
+            "algorithmic_flops_per_launch": flops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: timing the oracle (~{args.cpu_budget_s:.0f} s)")
+        gpu_out = out.to(torch.float64).cpu().numpy()
+        record["cpu_baseline"] = prefill_cpu_baseline(w, gpu_out, args.cpu_budget_s)
+        log(f"cpu baseline: {record['cpu_baseline']['sample']}")
+    print(json.dumps(record), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +257,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None,
                     help="tokens per split-KV partition (default: the workload's, else the library's)")
     ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--path", choices=["decode", "prefill"], default="decode",
+                    help="decode (the default step) or one chunked-prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -136,6 +294,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 3}), flush=True)
         return 0
+
+    if args.path == "prefill":
+        return run_prefill(args)
 
     log(f"building workload {args.config}")
     t0 = time.perf_counter()

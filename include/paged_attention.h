@@ -3,8 +3,9 @@
  *
  * The library implements the data-parallel hot path of PagedAttention on one MI355X:
  * decode-phase attention over a KV cache cut into fixed 16-token blocks that sit
- * anywhere in a physical pool, the slot write that stores a new token's K/V, and the
- * block copy behind copy-on-write of shared blocks.
+ * anywhere in a physical pool, the slot write that stores a new token's K/V (also into
+ * an fp8 cache, quantising), the block copy behind copy-on-write of shared blocks, and
+ * attention of several new tokens per sequence (chunked prefill) over the same cache.
  *
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers owned by the caller (allocated with
@@ -64,12 +65,12 @@ typedef enum {
  *   q_dtype, kv_dtype, out_dtype   pa_dtype_t codes; supported (q, kv, out):
  *                       (F32,F32,F32) (F16,F16,F16|F32) (BF16,BF16,BF16|F32)
  *                       (BF16,FP8_E4M3,BF16|F32)
- *   partition_size      0 (default): the KV work is cut into chunks balanced over the
- *                       device: each workgroup starts with an equal static chunk (about
- *                       70% of the work) and then takes small chunks as it finishes, so
- *                       faster compute units do more. A sequence is cut only where a
- *                       chunk ends. Otherwise a multiple of 16 (tokens): every chunk is
- *                       that long (fixed-size split-KV partitions, all taken on demand),
+ *   partition_size      0 (default): the KV work of the whole batch (16-token blocks of
+ *                       every sequence and kv head) is cut into equal contiguous chunks,
+ *                       one per workgroup of a fixed grid, whatever the length mix; a
+ *                       sequence is cut only where a chunk ends. Otherwise a multiple of
+ *                       16 (tokens): every chunk is that long (fixed-size split-KV
+ *                       partitions, taken from a counter by whichever workgroup is free),
  *                       so no piece of a sequence is longer. A call whose chunks could
  *                       exceed 16384 is rejected (UNSUPPORTED). The cut points depend on
  *                       the lengths only, so results are bitwise reproducible. */
@@ -139,6 +140,64 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
                       const int32_t* block_tables, const int32_t* context_lens,
                       int32_t max_context_len, float scale, float k_scale, float v_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Shape of one multi-token query call (pa_prefill).
+ *   batch               B, sequences; 0 is allowed (no-op)
+ *   num_query_tokens    Tq, query rows of all sequences together (= query_start[B])
+ *   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq
+ *                       as in pa_decode_desc_t (G in {1, 2, 4, 8}, d in {64, 128},
+ *                       block_size 16)
+ *   q_dtype, kv_dtype, out_dtype   supported (q, kv, out): (F16,F16,F16|F32)
+ *                       (BF16,BF16,BF16|F32) (BF16,FP8_E4M3,BF16|F32); fp32 K/V is not
+ *                       supported here (UNSUPPORTED) */
+typedef struct {
+  int32_t batch;
+  int32_t num_query_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t q_dtype;
+  int32_t kv_dtype;
+  int32_t out_dtype;
+} pa_prefill_desc_t;
+
+/* Attention of several new query tokens per sequence over the paged KV cache: the
+ * kernel side of chunked prefill (a long prompt prefilled a chunk per step) and of a
+ * prefix-cache hit that prefills only the uncached tail (LLM KV cache serving-engine
+ * article, sections 3 and 4). The new tokens' K/V must already be in the cache (slot
+ * write first).
+ *
+ * Defines: sequence b has L = context_lens[b] cached tokens, the last
+ * n = query_start[b+1] - query_start[b] of which are its query tokens; query token i
+ * (row query_start[b] + i of q and out) sits at position p = L - n + i and, for each query
+ * head h (kv head g = h / G),
+ *   s_t = scale * k_scale * dot(q[row][h], K_t)           0 <= t <= p
+ *   out[row][h] = v_scale * sum_t softmax(s)_t * V_t
+ * with the blockwise softmax merge of pa_decode (n = 1 is a decode step). Rows with p < 0
+ * (n > L) attend over nothing and are zero. Positions >= L are never read into the
+ * result, whatever the slots hold.
+ *
+ * Arguments (device pointers unless noted):
+ *   out            [Tq, Hq, d] out_dtype, written for the first min(n, max_query_len)
+ *                  rows of each sequence
+ *   q              [Tq, Hq, d] q_dtype
+ *   k_pool, v_pool [N, 16, Hkv, d] kv_dtype
+ *   block_tables   [B, maxb] int32; entries past ceil(L/16) are ignored
+ *   context_lens   [B] int32, each in [0, maxb*16] (larger values are clamped)
+ *   query_start    [B + 1] int32, non-decreasing from 0 to Tq
+ *   max_query_len  host int >= every n; sizes the launch (no device sync); at most
+ *                  min(Tq, maxb*16)
+ *   scale, k_scale, v_scale   host floats, as for pa_decode
+ * No workspace. One kernel is enqueued. All pointers must be 16-byte aligned (the int32
+ * arrays 4-byte). */
+pa_status_t pa_prefill(const pa_prefill_desc_t* desc, void* out, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start,
+                       int32_t max_query_len, float scale, float k_scale, float v_scale,
+                       void* stream);
 
 /* Slot write of new tokens (reshape_and_cache): a generated token occupies one slot
  * (vLLM-PagedAttention与连续批处理技术拆解, section 3.1). For each t < num_tokens with

@@ -1,4 +1,5 @@
-"""MI355X-native paged decode attention: Python binding of libpa.so.
+"""MI355X-native paged attention (decode and multi-token queries): Python binding of
+libpa.so.
 
 The names mirror the C ABI in include/paged_attention.h. Each function only marshals
 arguments (torch tensors -> device pointers, dtype codes, the current HIP stream) and
@@ -6,7 +7,8 @@ calls the library; every step of the computation runs in the HIP kernels. If the
 library is not built the calls raise; there is no fallback path.
 """
 from .binding import (  # noqa: F401
-    PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PaError, DecodeDesc, lib_path, load_library,
+    PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PaError, DecodeDesc, PrefillDesc, lib_path,
+    load_library,
     pa_abi_version, pa_status_string, pa_decode_max_chunks, decode_workspace, pa_decode_workspace_bytes,
-    pa_decode, pa_cache_write, pa_cache_write_fp8, pa_block_copy,
+    pa_decode, pa_prefill, pa_cache_write, pa_cache_write_fp8, pa_block_copy,
 )

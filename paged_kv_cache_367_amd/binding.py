@@ -32,6 +32,12 @@ class DecodeDesc(ctypes.Structure):
         "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype", "partition_size")]
 
 
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_query_tokens", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+        "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_dtype", "out_dtype")]
+
+
 def load_library():
     """Load libpa.so once; raises if it has not been built."""
     global _LIB
@@ -54,6 +60,8 @@ def load_library():
     lib.pa_decode_workspace_bytes.argtypes = [D, I32]
     lib.pa_decode.restype = I32
     lib.pa_decode.argtypes = [D, P, P, P, P, P, P, I32, F, F, F, P, SZ, P]
+    lib.pa_prefill.restype = I32
+    lib.pa_prefill.argtypes = [ctypes.POINTER(PrefillDesc), P, P, P, P, P, P, P, I32, F, F, F, P]
     lib.pa_cache_write.restype = I32
     lib.pa_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P]
     lib.pa_cache_write_fp8.restype = I32
@@ -158,6 +166,38 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_le
                        _stream(stream))
     if st != 0:
         raise PaError(st, "pa_decode")
+    return out
+
+
+def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+               max_query_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+               stream=None):
+    """Multi-token causal attention into `out` [Tq, Hq, d] for packed query rows q
+    [Tq, Hq, d]; sequence b owns rows query_start[b] .. query_start[b+1] - 1 (int32
+    [B + 1]), the last tokens of its context_lens[b] cached ones."""
+    import torch
+    lib = load_library()
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool differ in shape or dtype")
+    if out.shape != q.shape or q.dim() != 3:
+        raise ValueError("q and out must be [num_query_tokens, num_q_heads, head_dim]")
+    B = context_lens.shape[0]
+    if query_start.shape != (B + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("query_start must be [batch + 1], block_tables [batch, max_blocks]")
+    Tq, Hq, d = q.shape
+    N, bs, Hkv, dk = k_pool.shape
+    if dk != d:
+        raise ValueError("head_dim of q and the pool differ")
+    desc = PrefillDesc(B, Tq, Hq, Hkv, d, bs, N, block_tables.shape[1], dtype_code(q),
+                       dtype_code(k_pool), dtype_code(out))
+    st = lib.pa_prefill(ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"),
+                        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                        _dev(block_tables, "block_tables", torch.int32),
+                        _dev(context_lens, "context_lens", torch.int32),
+                        _dev(query_start, "query_start", torch.int32), int(max_query_len),
+                        float(scale), float(k_scale), float(v_scale), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_prefill")
     return out
 
 

@@ -20,7 +20,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 LIB = os.path.join(PKG, "libpa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["csrc/pa_api.cpp", "csrc/pa_decode.hip", "csrc/pa_cache_ops.hip"]
+SOURCES = ["csrc/pa_api.cpp", "csrc/pa_decode.hip", "csrc/pa_prefill.hip",
+           "csrc/pa_cache_ops.hip"]
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

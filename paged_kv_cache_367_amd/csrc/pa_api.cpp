@@ -205,6 +205,70 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
   return PA_OK;
 }
 
+pa_status_t pa_prefill(const pa_prefill_desc_t* desc, void* out, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start,
+                       int32_t max_query_len, float scale, float k_scale, float v_scale,
+                       void* stream) {
+  const pa_prefill_desc_t* d = desc;
+  if (!d) return PA_ERR_NULL;
+  if (d->batch < 0 || d->num_query_tokens < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->head_dim <= 0 || d->block_size <= 0 || d->num_blocks <= 0 ||
+      d->max_blocks_per_seq <= 0 || max_query_len < 0)
+    return PA_ERR_SHAPE;
+  if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype) || !valid_dtype(d->out_dtype))
+    return PA_ERR_DTYPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int group = d->num_q_heads / d->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (d->block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->kv_dtype == PA_F32 || !supported_combo(d->q_dtype, d->kv_dtype, d->out_dtype))
+    return PA_ERR_UNSUPPORTED;
+  if (max_query_len > d->num_query_tokens ||
+      (int64_t)max_query_len > (int64_t)d->max_blocks_per_seq * pa::kBlockTokens)
+    return PA_ERR_SHAPE;
+  const int64_t block_bytes =
+      (int64_t)pa::kBlockTokens * d->num_kv_heads * d->head_dim * dtype_bytes(d->kv_dtype);
+  if (block_bytes > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->max_blocks_per_seq > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int tq = pa::prefill_tile_tokens(group);
+  const int64_t tiles = ((int64_t)max_query_len + tq - 1) / tq;
+  const int64_t groups = ((int64_t)d->batch * d->num_kv_heads + 7) / 8;
+  if (groups * tiles * 8 > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (d->batch == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_ALIGN;
+  if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_SHAPE;
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.batch = d->batch;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.num_blocks = d->num_blocks;
+  a.max_blocks_per_seq = d->max_blocks_per_seq;
+  a.num_query_tokens = d->num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.num_q_tiles = (int32_t)tiles;
+  a.num_workgroups = (int32_t)(groups * tiles * 8);
+  a.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
+  if (pa::launch_prefill(d->q_dtype, d->kv_dtype, d->out_dtype, d->head_dim, group, a,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
 static pa_status_t check_cache_args(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                     int32_t num_blocks, int32_t kv_dtype, int64_t* row_bytes) {
   if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)

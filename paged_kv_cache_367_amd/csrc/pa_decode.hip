@@ -44,43 +44,17 @@
 #include <stdint.h>
 
 #include "../../include/paged_attention.h"
+#include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 namespace {
 
-constexpr int kWave = 64;
 #ifndef PA_RING_BYTES
 #define PA_RING_BYTES 16384
 #endif
 constexpr int kRingBytes = PA_RING_BYTES;  // K and V bytes in flight per wave (ring depth)
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x1 __attribute__((ext_vector_type(1)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-template <int T> struct Enc;
-template <> struct Enc<PA_F32> { static constexpr int bytes = 4; };
-template <> struct Enc<PA_F16> { static constexpr int bytes = 2; };
-template <> struct Enc<PA_BF16> { static constexpr int bytes = 2; };
-template <> struct Enc<PA_FP8_E4M3> { static constexpr int bytes = 1; };
-
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// DPP lane moves inside 16-lane rows.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
 // Row reductions use four DPP steps, quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 // row_half_mirror and row_mirror: after them every lane of a 16-lane row holds the
 // row's result.
@@ -130,31 +104,6 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// A value the whole wave agrees on (an LDS word read at a uniform address), marked as
-// such so that what is derived from it stays in scalar registers; without this the
-// compiler wraps every load whose descriptor depends on it in a per-lane loop.
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Make LDS writes of this wave visible to its own later LDS reads from other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), other counters untouched
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Raw buffer loads: the block base lives in a scalar descriptor, each lane adds a
-// constant 32-bit offset. Offsets at or beyond `bytes` read as zero without touching
-// memory, which gives past-the-end prefetches for free (bytes = 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
-}
 template <int BYTES> struct VChunk;
 template <> struct VChunk<16> {
   using type = u32x4;
@@ -176,22 +125,6 @@ template <> struct VChunk<4> {
     return v;
   }
 };
-
-// fp32 -> bf16, round to nearest even (the hardware conversion of CDNA4)
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-
-template <int OT>
-__device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
-  if constexpr (OT == PA_F32) {
-    static_cast<float*>(out)[idx] = x;
-  } else if constexpr (OT == PA_F16) {
-    static_cast<_Float16*>(out)[idx] = (_Float16)x;
-  } else {
-    static_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(x);
-  }
-}
 
 // Matrix-core P.V (16-bit and fp8 K/V). V words of one token row, as pairs of 16-bit values
 // in the MFMA's element type (fp8 widened exactly to bf16).
@@ -275,28 +208,6 @@ __device__ __forceinline__ u32x2 round_pack4(const float (&p)[4], float (&pr)[4]
     return a;
   }
 }
-// Max and sum over the four row groups of a column: lanes l, l ^ 16, l ^ 32, l ^ 48.
-// v_permlane16_swap / v_permlane32_swap exchange rows 0<->1, 2<->3 and the two halves,
-// so with both operands equal, the pair returned holds each lane's value and its
-// partner's, in some order.
-__device__ __forceinline__ float xrow_max(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  x = a > b ? a : b;
-  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                   false);
-  const float c = __uint_as_float(r2[0]), d = __uint_as_float(r2[1]);
-  return c > d ? c : d;
-}
-__device__ __forceinline__ float xrow_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                   false);
-  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
-}
 // DPP quad broadcast: every lane gets the value of lane I of its quad
 template <int I>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -325,10 +236,6 @@ __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int st = 1; st < kWave; st <<= 1) x = fmaxf(x, __shfl_xor(x, st));
   return x;
-}
-
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
 }
 
 // Register allocation target: 8 waves per CU (2 per SIMD), i.e. at most 256 VGPRs.

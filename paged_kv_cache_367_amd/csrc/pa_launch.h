@@ -1,5 +1,6 @@
 // pa_launch.h - internal launch interface between the C ABI (pa_api.cpp) and the HIP
-// kernels (pa_decode.hip, pa_cache_ops.hip). Not installed; not part of the ABI.
+// kernels (pa_decode.hip, pa_prefill.hip, pa_cache_ops.hip). Not installed; not part of
+// the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -96,6 +97,34 @@ struct MergeArgs {
   float v_scale;
 };
 
+// Multi-token queries (pa_prefill). A workgroup of kPrefillWaves waves owns one
+// (sequence, kv head, tile of query tokens); each wave holds kPrefillRowGroups groups of
+// 16 (token, head) rows, so a tile has 16 * kPrefillWaves * kPrefillRowGroups / G tokens.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowGroups = 2;
+inline int prefill_tile_tokens(int group) { return 16 * kPrefillWaves * kPrefillRowGroups / group; }
+
+struct PrefillArgs {
+  void* out;                    // [Tq, Hq, d] out dtype
+  const void* q;                // [Tq, Hq, d] q dtype (16-bit)
+  const void* k_pool;           // [N, 16, Hkv, d]
+  const void* v_pool;
+  const int32_t* block_tables;  // [B, maxb]
+  const int32_t* context_lens;  // [B]
+  const int32_t* query_start;   // [B + 1]
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_query_tokens;     // Tq
+  int32_t max_query_len;        // rows past it in a sequence are not computed
+  int32_t num_q_tiles;          // query tiles per (sequence, kv head)
+  int32_t num_workgroups;       // ceil(B * Hkv / 8) * num_q_tiles * 8
+  float qk_scale_log2;          // scale * k_scale * log2(e)
+  float v_scale;
+};
+
 // Waves per workgroup for Hkv kv heads: the largest of 8, 4, 2, 1 dividing Hkv.
 inline int group_waves(int num_kv_heads) {
   for (int nw = kMaxGroupWaves; nw > 1; nw >>= 1)
@@ -107,6 +136,9 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, int out_dtype, int head_dim,
                          const DecodeArgs& args, int group_waves, hipStream_t stream);
 hipError_t launch_merge(int out_dtype, int head_dim, int group, const MergeArgs& args,
                         hipStream_t stream);
+
+hipError_t launch_prefill(int q_dtype, int kv_dtype, int out_dtype, int head_dim, int group,
+                          const PrefillArgs& args, hipStream_t stream);
 
 hipError_t launch_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                               const int64_t* slot_mapping, int32_t num_tokens,

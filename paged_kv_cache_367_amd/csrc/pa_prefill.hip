@@ -1,0 +1,438 @@
+// pa_prefill.hip - attention of several new query tokens per sequence over a block-paged
+// KV cache (chunked prefill, or the tail left after a prefix-cache hit), gfx950 (CDNA4).
+//
+// What is computed (LLM KV cache serving-engine article, sections 3 and 4; softmax and
+// block table as in vLLM-PagedAttention与连续批处理技术拆解, sections 3.1-3.3): sequence b
+// holds L tokens in its paged cache, the last n of which are its new query tokens, already
+// written by the slot write. Query token i sits at position L - n + i and attends over
+// positions [0, L - n + i] (causal among the new tokens); a position below zero (n > L)
+// attends over nothing and gives a zero row.
+//
+// How it maps onto CDNA4
+//   * A workgroup of 4 waves owns one (sequence, kv head, tile of TQ query tokens). Its
+//     rows are (token, head) pairs, row r = token r / G, head r % G, so the G query heads
+//     that share a kv head share every K/V byte: each wave owns RG groups of 16 rows.
+//   * K/V are staged through LDS 64 tokens (4 blocks) at a time, double-buffered: the
+//     global loads of the next tile are in flight while the current one is computed. fp8
+//     rows are widened to bf16 (exactly) on the way in, so the matrix cores see one
+//     layout. LDS rows are padded by 16 bytes to spread the banks.
+//   * Scores run on the matrix cores as K.Q^T (v_mfma_f32_16x16x32_{bf16,f16}): lane
+//     (n, kq) = (lane % 16, lane / 16) ends with the scores of tokens 4kq .. 4kq+3 of each
+//     16-token subtile for row n, which is, two subtiles at a time, exactly the A-operand
+//     layout P takes in P.V, so P never leaves registers.
+//   * Online softmax per row (running max m and normaliser l, rescaled when m moves).
+//     The matrix cores take p in 16 bits. fp16 (relative rounding 2^-11) is used as is,
+//     with l summing the rounded values so the output stays an exact weighted average of
+//     V rows. bf16 rounds p by up to 2^-9, which on rows that attend over a few tokens
+//     moves the output by a visible fraction of the spread of V; for bf16 K/V p is
+//     therefore split into hi = bf16(p) and lo = bf16(p - hi) and P.V takes both
+//     (weights exact to about 2^-17, at twice the P.V matrix work). fp8 K/V, whose own
+//     rounding is far coarser, takes the single bf16 pass.
+//   * Tiles wholly at or before the tile's first query position need no mask; the rest
+//     mask positions past each row's own.
+//   * Workgroup ids are dealt so that all query tiles of one (sequence, kv head) land on
+//     the same XCD (workgroups go to the 8 XCDs round-robin) and share its L2; within a
+//     pair, later tiles (longer key ranges) start first.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/paged_attention.h"
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+constexpr int kTileTokens = 64;                      // K/V tokens per LDS tile
+constexpr int kPrefillThreads = kPrefillWaves * kWave;
+
+// One 16x16x32 MFMA in the 16-bit type CT: acc += A * B.
+template <int CT>
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 acc) {
+  if constexpr (CT == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// Two floats rounded to CT (nearest even) and packed, a in the low half; ra, rb get the
+// rounded values.
+template <int CT>
+__device__ __forceinline__ uint32_t pack2(float a, float b, float& ra, float& rb) {
+  if constexpr (CT == PA_F16) {
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    ra = (float)ha;
+    rb = (float)hb;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           (uint32_t)__builtin_bit_cast(uint16_t, hb) << 16;
+  } else {
+    const bf16x2 h = {(__bf16)a, (__bf16)b};
+    const uint32_t w = __builtin_bit_cast(uint32_t, h);
+    ra = __uint_as_float(w << 16);
+    rb = __uint_as_float(w & 0xffff0000u);
+    return w;
+  }
+}
+
+// N consecutive outputs from idx (16-byte aligned for 16-bit outputs of N = 8, 8-byte for
+// N = 4), converted to the output type.
+template <int OT, int N>
+__device__ __forceinline__ void store_run(void* out, size_t idx, const float (&x)[N]) {
+  if constexpr (OT == PA_F32) {
+    float* o = static_cast<float*>(out) + idx;
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<f32x4*>(o + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      float ra, rb;
+      w[i] = pack2<OT>(x[2 * i], x[2 * i + 1], ra, rb);
+    }
+    uint16_t* o = static_cast<uint16_t*>(out) + idx;
+    if constexpr (N == 8)
+      *reinterpret_cast<u32x4*>(o) = u32x4{w[0], w[1], w[2], w[3]};
+    else
+      *reinterpret_cast<u32x2*>(o) = u32x2{w[0], w[1]};
+  }
+}
+
+template <int KV, int OT, int D, int G, int RG>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
+  constexpr int CT = KV == PA_F16 ? PA_F16 : PA_BF16;  // element type of the MFMAs
+  constexpr bool SPLIT = KV == PA_BF16;                // p as hi + lo bf16 parts
+  constexpr int KB = Enc<KV>::bytes;
+  constexpr int ROWB = D * KB;                   // pool bytes of one token row, one kv head
+  constexpr int LROW = D * 2 + 16;               // LDS bytes of one token row (16-bit, padded)
+  constexpr int ROWS = kPrefillWaves * RG * 16;  // (token, head) rows of the workgroup
+  constexpr int TQ = ROWS / G;                   // query tokens of the workgroup
+  constexpr int NC = D / 32;                     // 32-dim steps of a score MFMA chain
+  constexpr int DPL = D / 16;                    // output dims per lane and 16-row group
+  constexpr int CPR = ROWB / 16;                 // 16-byte pool chunks per token row
+  constexpr int CPT = kTileTokens * CPR / kPrefillThreads;  // chunks per thread and tile
+  static_assert(CPT * kPrefillThreads == kTileTokens * CPR, "tile staging layout");
+  static_assert(ROWS % G == 0 && 16 % G == 0, "rows hold whole tokens");
+  using VW = typename std::conditional<DPL == 8, u32x4, u32x2>::type;  // DPL 16-bit values
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kTileTokens * LROW];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kTileTokens * LROW];
+
+  // ---- which (sequence, kv head, query tile): id = ((group * tiles) + tile') * 8 + x,
+  // pair = group * 8 + x, tile = tiles - 1 - tile'
+  const int id = blockIdx.x;
+  const int x8 = id & 7, rest = id >> 3;
+  const int pair = (rest / a.num_q_tiles) * 8 + x8;
+  if (pair >= a.batch * a.num_kv_heads) return;
+  const int tile = a.num_q_tiles - 1 - rest % a.num_q_tiles;
+  const int b = pair / a.num_kv_heads, kvh = pair - b * a.num_kv_heads;
+  // the sequence's rows, kept inside [0, Tq) whatever query_start holds; rows past
+  // max_query_len are not computed, though they still count in the positions
+  const int Tq = a.num_query_tokens;
+  int qs0 = a.query_start[b], qs1 = a.query_start[b + 1];
+  qs0 = qs0 < 0 ? 0 : (qs0 < Tq ? qs0 : Tq);
+  qs1 = qs1 < qs0 ? qs0 : (qs1 < Tq ? qs1 : Tq);
+  const int n = qs1 - qs0;
+  const int nr = n < a.max_query_len ? n : a.max_query_len;   // rows computed
+  const int t0 = tile * TQ;
+  if (t0 >= nr) return;
+  const int cap = a.max_blocks_per_seq * kBlockTokens;
+  int L = a.context_lens[b];
+  L = L < 0 ? 0 : (L < cap ? L : cap);
+  const int nb = (L + kBlockTokens - 1) / kBlockTokens;
+  const int pos0 = L - n;                                  // position of query token 0
+  const int last_pos = pos0 + (t0 + TQ < nr ? t0 + TQ : nr) - 1;
+  const int first_pos = pos0 + t0;
+  const int ntiles = last_pos < 0 ? 0 : last_pos / kTileTokens + 1;
+  const int nfull = first_pos < 0 ? 0 : (first_pos + 1) / kTileTokens;  // tiles needing no mask
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int li = lane & 15, lk = lane >> 4;
+  const int Hq = a.num_q_heads;
+
+  // ---- q rows as the B operand: lane (li, lk) holds dims 32c + 8lk .. +7 of row li
+  u32x4 qop[RG][NC];
+  int qpos[RG];                                            // position of row li's token
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r = (wave * RG + rg) * 16 + li;
+    const int t = t0 + r / G, h = r % G;
+    const bool ok = t < nr;
+    qpos[rg] = pos0 + (ok ? t : nr - 1);                   // padding rows copy a real one
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
+                          ((size_t)(qs0 + (ok ? t : 0)) * Hq + (size_t)kvh * G + h) * D * 2;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qop[rg][c] = ok ? *reinterpret_cast<const u32x4*>(qrow + (32 * c + 8 * lk) * 2)
+                      : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- K/V staging: thread tid moves chunks tid + 256 i (token ci / CPR, column ci % CPR)
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  const size_t tok_stride = (size_t)a.num_kv_heads * ROWB;
+  const size_t blk_stride = kBlockTokens * tok_stride;
+  const uint8_t* const kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)kvh * ROWB;
+  const uint8_t* const vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)kvh * ROWB;
+  // block ids of a tile's 4 blocks (-1 past the sequence); the same for every lane
+  auto load_ids = [&](int kt, int (&ids)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = kt * 4 + i;
+      ids[i] = __builtin_amdgcn_readfirstlane(j < nb ? bt[j] : -1);
+    }
+  };
+  // positions at or past L read as zero, so that stale or NaN slots never meet a p = 0
+  auto stage = [&](int kt, const int (&ids)[4], u32x4 (&kr)[CPT], u32x4 (&vr)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + kPrefillThreads * i;
+      const int tok = ci / CPR, col = ci % CPR;
+      const int blk = tok / kBlockTokens;
+      const int pid = blk == 0 ? ids[0] : blk == 1 ? ids[1] : blk == 2 ? ids[2] : ids[3];
+      const int pos = kt * kTileTokens + tok;
+      const bool ok = pos < L && (unsigned)pid < (unsigned)a.num_blocks;
+      const size_t off = (size_t)pid * blk_stride + (size_t)(tok % kBlockTokens) * tok_stride +
+                         (size_t)col * 16;
+      kr[i] = vr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok) {
+        kr[i] = *reinterpret_cast<const u32x4*>(kpool + off);
+        vr[i] = *reinterpret_cast<const u32x4*>(vpool + off);
+      }
+    }
+  };
+  auto to_lds = [&](int buf, const u32x4 (&kr)[CPT], const u32x4 (&vr)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + kPrefillThreads * i;
+      const int tok = ci / CPR, col = ci % CPR;
+      if constexpr (KV == PA_FP8_E4M3) {
+        // 16 E4M3 values -> 16 bf16 (exact)
+        uint32_t kw[8], vw[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kw[2 * w] = __builtin_bit_cast(uint32_t,
+                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, false));
+          kw[2 * w + 1] = __builtin_bit_cast(uint32_t,
+                                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, true));
+          vw[2 * w] = __builtin_bit_cast(uint32_t,
+                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, false));
+          vw[2 * w + 1] = __builtin_bit_cast(uint32_t,
+                                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, true));
+        }
+        uint8_t* kd = &s_k[buf][tok * LROW + col * 32];
+        uint8_t* vd = &s_v[buf][tok * LROW + col * 32];
+        *reinterpret_cast<u32x4*>(kd) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+        *reinterpret_cast<u32x4*>(kd + 16) = u32x4{kw[4], kw[5], kw[6], kw[7]};
+        *reinterpret_cast<u32x4*>(vd) = u32x4{vw[0], vw[1], vw[2], vw[3]};
+        *reinterpret_cast<u32x4*>(vd + 16) = u32x4{vw[4], vw[5], vw[6], vw[7]};
+      } else {
+        *reinterpret_cast<u32x4*>(&s_k[buf][tok * LROW + col * 16]) = kr[i];
+        *reinterpret_cast<u32x4*>(&s_v[buf][tok * LROW + col * 16]) = vr[i];
+      }
+    }
+  };
+
+  // ---- running state: row li's max m (log2 units) and partial normaliser l (this lane's
+  // tokens), and acc[rg][e]: lane (j, g) holds rows 4g + v, dim DPL*j + e
+  float m[RG], l[RG];
+  f32x4 acc[RG][DPL];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    m[rg] = neg_inf();
+    l[rg] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[rg][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  auto compute = [&](int buf, int kt) {
+    const uint8_t* Kt = s_k[buf];
+    const uint8_t* Vt = s_v[buf];
+    // scores: sc[rg][s][v] = row li of group rg against token 16s + 4lk + v
+    f32x4 sc[RG][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 kop[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kop[c] = *reinterpret_cast<const u32x4*>(Kt + (16 * s + li) * LROW + (32 * c + 8 * lk) * 2);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) z = mfma32<CT>(kop[c], qop[rg][c], z);
+        sc[rg][s] = z;
+      }
+    }
+    const bool masked = kt >= nfull;
+    u32x4 aop[RG][2];                      // P as the A operand, two subtiles per MFMA
+    u32x4 alo[SPLIT ? RG : 1][2];          // the low parts of P (bf16 K/V)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      float sv[4][4];
+      float bm = neg_inf();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = sc[rg][s][v] * a.qk_scale_log2;
+          if (masked) x = kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] ? x : neg_inf();
+          sv[s][v] = x;
+          bm = x > bm ? x : bm;
+        }
+      const float mn = xrow_max(bm > m[rg] ? bm : m[rg]);
+      const float base = mn == neg_inf() ? 0.0f : mn;
+      const float al = m[rg] == mn ? 1.0f : fast_exp2(m[rg] - base);
+      float ls = 0.0f;
+#pragma unroll
+      for (int pi = 0; pi < 2; ++pi) {
+        uint32_t w[4], wl[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; v += 2) {
+            const float pa = fast_exp2(sv[2 * pi + h][v] - base);
+            const float pb = fast_exp2(sv[2 * pi + h][v + 1] - base);
+            float ra, rb;
+            w[2 * h + v / 2] = pack2<CT>(pa, pb, ra, rb);
+            if constexpr (SPLIT) {
+              float la, lb;
+              wl[2 * h + v / 2] = pack2<CT>(pa - ra, pb - rb, la, lb);
+              ls += (ra + la) + (rb + lb);
+            } else {
+              ls += ra + rb;
+            }
+          }
+        aop[rg][pi] = u32x4{w[0], w[1], w[2], w[3]};
+        if constexpr (SPLIT) alo[rg][pi] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+      }
+      l[rg] = l[rg] * al + ls;
+      m[rg] = mn;
+      // rows 4lk + v of the accumulator take the factor of row 4lk + v (held by lane 4lk + v)
+      if (__builtin_amdgcn_ballot_w64(al != 1.0f) != 0) {
+        float alv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) alv[v] = __shfl(al, 4 * lk + v);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[rg][e][v] *= alv[v];
+      }
+    }
+    // P.V: k-slot 8lk + e is token 32pi + 4lk + e (e < 4) or 32pi + 16 + 4lk + e - 4
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) {
+      VW vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 32 * pi + (e < 4 ? 4 * lk + e : 16 + 4 * lk + e - 4);
+        vr[e] = *reinterpret_cast<const VW*>(Vt + tok * LROW + li * DPL * 2);
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int w = e >> 1;
+        const u32x4 bop = {__builtin_amdgcn_perm(vr[1][w], vr[0][w], sel),
+                           __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel),
+                           __builtin_amdgcn_perm(vr[5][w], vr[4][w], sel),
+                           __builtin_amdgcn_perm(vr[7][w], vr[6][w], sel)};
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          acc[rg][e] = mfma32<CT>(aop[rg][pi], bop, acc[rg][e]);
+          if constexpr (SPLIT) acc[rg][e] = mfma32<CT>(alo[rg][pi], bop, acc[rg][e]);
+        }
+      }
+    }
+  };
+
+  // ---- the key loop: stage tile kt + 1 (ids one tile further ahead) while computing kt
+  int ids[4];
+  u32x4 kr[CPT], vr[CPT];
+  if (ntiles > 0) {
+    load_ids(0, ids);
+    stage(0, ids, kr, vr);
+    to_lds(0, kr, vr);
+    if (ntiles > 1) load_ids(1, ids);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const bool more = kt + 1 < ntiles;
+    if (more) stage(kt + 1, ids, kr, vr);
+    if (kt + 2 < ntiles) load_ids(kt + 2, ids);
+    compute(kt & 1, kt);
+    if (more) to_lds((kt + 1) & 1, kr, vr);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane (j, lk) writes rows 4lk + v, dims DPL*j .. DPL*j+DPL-1
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const float lt = xrow_sum(l[rg]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float lr = __shfl(lt, 4 * lk + v);
+      const int r = (wave * RG + rg) * 16 + 4 * lk + v;
+      const int t = t0 + r / G, h = r % G;
+      if (t >= nr) continue;
+      const float inv = lr > 0.0f ? a.v_scale / lr : 0.0f;
+      float o[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = acc[rg][e][v] * inv;
+      store_run<OT, DPL>(a.out, ((size_t)(qs0 + t) * Hq + (size_t)kvh * G + h) * D + DPL * li, o);
+    }
+  }
+}
+
+template <int KV, int OT, int D, int G>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  prefill_kernel<KV, OT, D, G, kPrefillRowGroups><<<dim3(a.num_workgroups), dim3(kPrefillThreads),
+                                                   0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int KV, int OT, int D>
+hipError_t prefill_group(int group, const PrefillArgs& a, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_prefill_t<KV, OT, D, 1>(a, stream);
+    case 2: return launch_prefill_t<KV, OT, D, 2>(a, stream);
+    case 4: return launch_prefill_t<KV, OT, D, 4>(a, stream);
+    case 8: return launch_prefill_t<KV, OT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KV, int OT>
+hipError_t prefill_dim(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return prefill_group<KV, OT, 64>(group, a, stream);
+    case 128: return prefill_group<KV, OT, 128>(group, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int q_dtype, int kv_dtype, int out_dtype, int head_dim, int group,
+                          const PrefillArgs& a, hipStream_t stream) {
+  if (q_dtype == PA_F16 && kv_dtype == PA_F16) {
+    if (out_dtype == PA_F16) return prefill_dim<PA_F16, PA_F16>(head_dim, group, a, stream);
+    if (out_dtype == PA_F32) return prefill_dim<PA_F16, PA_F32>(head_dim, group, a, stream);
+  }
+  if (q_dtype == PA_BF16 && kv_dtype == PA_BF16) {
+    if (out_dtype == PA_BF16) return prefill_dim<PA_BF16, PA_BF16>(head_dim, group, a, stream);
+    if (out_dtype == PA_F32) return prefill_dim<PA_BF16, PA_F32>(head_dim, group, a, stream);
+  }
+  if (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3) {
+    if (out_dtype == PA_BF16)
+      return prefill_dim<PA_FP8_E4M3, PA_BF16>(head_dim, group, a, stream);
+    if (out_dtype == PA_F32) return prefill_dim<PA_FP8_E4M3, PA_F32>(head_dim, group, a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

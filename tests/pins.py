@@ -475,7 +475,8 @@ def _prefill(c, **kw):
     import oracle.prefill as pf
     args = dict(c, **kw)
     return pf.prefill_ref(args["q"], args["qs"], args["k"], args["v"], args["tables"],
-                          args["lens"], args["scale"], q_kind="bf16", kv_kind=args["kv"])
+                          args["lens"], args["scale"], q_kind="bf16", kv_kind=args["kv"],
+                          rows=args.get("rows"))
 
 
 def pin_prefill_one_token_is_decode():
@@ -552,6 +553,19 @@ def pin_prefill_sequences_independent():
     pert = _prefill(c, q=q2)
     assert np.array_equal(pert[:4], base[:4]) and np.array_equal(pert[9:], base[9:])
     assert not np.array_equal(pert[4:9], base[4:9])
+
+
+
+
+def pin_prefill_sampled_rows_equal_full():
+    """Computing a subset of rows gives those rows of the full result, and NaN elsewhere."""
+    c = _prefill_case([3, 9], kv="bf16", G=2, Hkv=2, d=64, seed=21)
+    full = _prefill(c)
+    rows = [0, 4, 11]
+    part = _prefill(c, rows=rows)
+    assert np.array_equal(part[rows], full[rows])
+    others = [r for r in range(full.shape[0]) if r not in rows]
+    assert np.isnan(part[others]).all()
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -138,3 +138,41 @@ def test_cache_ops_reject_before_launch(lib):
     assert lib.pa_block_copy(p, p, z, 3, 8, 128, 16, 100, pa.PA_BF16, None) == -1
     assert lib.pa_block_copy(p, p, p, 0, 8, 128, 16, 100, pa.PA_BF16, None) == 0
     assert lib.pa_block_copy(p, p, p, 3, 0, 128, 16, 100, pa.PA_BF16, None) == -2
+
+
+def _pdesc(**kw):
+    base = dict(batch=16, num_query_tokens=8192, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, num_blocks=5000, max_blocks_per_seq=512, q_dtype=pa.PA_BF16,
+                kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16)
+    base.update(kw)
+    return pa.PrefillDesc(*[base[f] for f, _ in pa.PrefillDesc._fields_])
+
+
+def _prefill(lib, desc, max_q=512, ptr=0x10000, qs_ptr=None, scale=0.088):
+    p = ctypes.c_void_p(ptr)
+    qs = p if qs_ptr is None else ctypes.c_void_p(qs_ptr)
+    return lib.pa_prefill(ctypes.byref(desc) if desc is not None else None, p, p, p, p, p, p, qs,
+                          max_q, scale, 1.0, 1.0, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("kv_dtype", pa.PA_F32, -4), ("q_dtype", pa.PA_F32, -4), ("head_dim", 96, -4),
+    ("block_size", 32, -4), ("num_q_heads", 30, -2), ("num_q_heads", 8 * 16, -4),
+    ("kv_dtype", 9, -3), ("out_dtype", pa.PA_F16, -4), ("num_blocks", 0, -2),
+    ("batch", -1, -2), ("num_query_tokens", -1, -2), ("num_query_tokens", 100, -2),
+    ("max_blocks_per_seq", 0, -2), ("max_blocks_per_seq", 16, -2),
+])
+def test_prefill_rejects_bad_descriptor(lib, field, value, code):
+    assert _prefill(lib, _pdesc(**{field: value})) == code
+
+
+def test_prefill_rejects_before_launch(lib):
+    assert _prefill(lib, None) == -1
+    assert _prefill(lib, _pdesc(), max_q=-1) == -2
+    assert _prefill(lib, _pdesc(), ptr=0) == -1
+    assert _prefill(lib, _pdesc(), qs_ptr=0) == -1                  # query_start missing
+    assert _prefill(lib, _pdesc(), ptr=0x10008) == -6
+    assert _prefill(lib, _pdesc(), qs_ptr=0x10002) == -6
+    assert _prefill(lib, _pdesc(), scale=float("inf")) == -2
+    assert _prefill(lib, _pdesc(batch=0)) == 0                      # nothing to do
+    assert _prefill(lib, _pdesc(), max_q=0) == 0

@@ -17,6 +17,12 @@ Workloads (shapes from the pages' examples, sizes from the five named configurat
   5  long-context fp8-E4M3 KV: B=16, L ~ U{16384..32768}, GQA 32/8, d=128, per-tensor
      scales, 512-token split-KV partitions.
 
+Multi-token queries (chunked prefill, prefix-cache tails): prefill_custom builds packed
+query rows over a scattered pool for explicit query and context lengths;
+chunked_prefill is the Llama-3-8B-shaped step of 16 prompts each prefilling its next
+512-token chunk (a token budget of 8192; the LLM KV cache serving-engine article,
+section 3, sweeps budgets of 512 to 8192), chunk index c ~ U{0..15}, so L = 512 (c + 1).
+
 Block size is 16 everywhere (vLLM-PagedAttention与连续批处理技术拆解, section 3.1).
 The pool layout is [num_blocks, block_size, kv_heads, head_dim] (AI vLLM: PagedAttention
 不够用了之后, the paged_attention sketch's docstring); K and V are separate pools.
@@ -387,3 +393,89 @@ def custom(*, batch, num_q_heads, num_kv_heads, head_dim, kv_dtype, q_dtype=None
     return _finish(f"custom_g{num_q_heads // num_kv_heads}_d{head_dim}_{kv_dtype}", 0,
                    SEED_BASE + 100 + seed, L, tables, N, num_q_heads, num_kv_heads, head_dim,
                    kv_dtype, qd, od, rngs, partition_size=partition_size)
+
+
+# ----------------------------------------------------------------------------- multi-token queries
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    kv_dtype: str
+    q_dtype: str
+    out_dtype: str
+    scale: float
+    k_scale: float
+    v_scale: float
+    context_lens: np.ndarray          # int32 [B]
+    query_start: np.ndarray           # int32 [B + 1]
+    block_tables: np.ndarray          # int32 [B, maxb], -1 padded
+    q: np.ndarray                     # storage [Tq, Hq, d]
+    k_pool: np.ndarray                # storage [N, bs, Hkv, d]
+    v_pool: np.ndarray
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.size)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start.astype(np.int64))
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.batch else 0
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+
+def prefill_custom(*, query_lens, context_lens, num_q_heads, num_kv_heads, head_dim,
+                   kv_dtype, q_dtype=None, out_dtype=None, seed=0, slack=0.10,
+                   name=None) -> PrefillWorkload:
+    """Packed query rows (query_lens[b] for sequence b) over a scattered pool holding
+    context_lens[b] tokens per sequence; the query tokens are the last ones of each."""
+    rngs = _children(200, seed)
+    L = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    n = np.asarray(query_lens, dtype=np.int64).reshape(-1)
+    if n.shape != L.shape:
+        raise ValueError("one query length per sequence")
+    nb = _nblocks(L)
+    N, tables = _scattered_pool(nb, rngs["placement"], slack)
+    qd = q_dtype or ("bf16" if kv_dtype == "fp8_e4m3" else kv_dtype)
+    od = out_dtype or qd
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = _normal_storage(rngs["q"], (int(qs[-1]), num_q_heads, head_dim), qd)
+    ks: list = []
+    vs: list = []
+    k_pool = _normal_storage(rngs["k"], (N, BLOCK_SIZE, num_kv_heads, head_dim), kv_dtype, ks)
+    v_pool = _normal_storage(rngs["v"], (N, BLOCK_SIZE, num_kv_heads, head_dim), kv_dtype, vs)
+    return PrefillWorkload(
+        name=name or f"prefill_g{num_q_heads // num_kv_heads}_d{head_dim}_{kv_dtype}",
+        seed=SEED_BASE + 200 + seed, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, num_blocks=N, kv_dtype=kv_dtype, q_dtype=qd, out_dtype=od,
+        scale=1.0 / math.sqrt(head_dim), k_scale=ks[0] if ks else 1.0,
+        v_scale=vs[0] if vs else 1.0, context_lens=L.astype(np.int32), query_start=qs,
+        block_tables=tables, q=q, k_pool=k_pool, v_pool=v_pool)
+
+
+def chunked_prefill(*, batch: int = 16, chunk: int = 512, max_chunks: int = 16,
+                    seed_offset: int = 0) -> PrefillWorkload:
+    """One chunked-prefill step of a Llama-3-8B-shaped layer (32 q heads over 8 kv heads,
+    d=128, bf16): `batch` prompts, each with c ~ U{0..max_chunks-1} chunks already cached
+    and its next `chunk` tokens as queries, so L = chunk * (c + 1) and n = chunk."""
+    rng = _children(201, seed_offset)["lengths"]
+    c = rng.integers(0, max_chunks, size=batch)
+    L = chunk * (c + 1)
+    return prefill_custom(query_lens=np.full(batch, chunk), context_lens=L, num_q_heads=32,
+                          num_kv_heads=8, head_dim=128, kv_dtype="bf16", seed=1 + seed_offset,
+                          name="chunked_prefill_llama3_8b_bf16")
