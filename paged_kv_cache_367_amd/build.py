@@ -45,11 +45,16 @@ def compile_source(src: str, verbose: bool = False, extra=()) -> str:
     return obj
 
 
+# Per-source flags. The prefill kernel keeps its MFMA accumulators in ordinary VGPRs
+# (no accumulator-register copies around the vector-ALU rescale; 2 waves per SIMD fit).
+EXTRA = {"csrc/pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libpa.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: compile_source(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: compile_source(s, verbose, EXTRA.get(s, ())), SOURCES))
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

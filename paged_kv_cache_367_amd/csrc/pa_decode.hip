@@ -104,28 +104,6 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-template <int BYTES> struct VChunk;
-template <> struct VChunk<16> {
-  using type = u32x4;
-  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-    return buf_load16(r, o);
-  }
-};
-template <> struct VChunk<8> {
-  using type = u32x2;
-  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-    return buf_load8(r, o);
-  }
-};
-template <> struct VChunk<4> {
-  using type = u32x1;
-  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-    u32x1 v;
-    v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, 0);
-    return v;
-  }
-};
-
 // Matrix-core P.V (16-bit and fp8 K/V). V words of one token row, as pairs of 16-bit values
 // in the MFMA's element type (fp8 widened exactly to bf16).
 template <int KV, int WORDS, typename VTy>

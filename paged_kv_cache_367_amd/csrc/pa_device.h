@@ -109,5 +109,28 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
 }
 
+// Loads of 16, 8 or 4 bytes per lane through a buffer descriptor.
+template <int BYTES> struct VChunk;
+template <> struct VChunk<16> {
+  using type = u32x4;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return buf_load16(r, o);
+  }
+};
+template <> struct VChunk<8> {
+  using type = u32x2;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return buf_load8(r, o);
+  }
+};
+template <> struct VChunk<4> {
+  using type = u32x1;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    u32x1 v;
+    v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, 0);
+    return v;
+  }
+};
+
 }  // namespace
 }  // namespace pa

@@ -25,9 +25,10 @@
 //     with l summing the rounded values so the output stays an exact weighted average of
 //     V rows. bf16 rounds p by up to 2^-9, which on rows that attend over a few tokens
 //     moves the output by a visible fraction of the spread of V; for bf16 K/V p is
-//     therefore split into hi = bf16(p) and lo = bf16(p - hi) and P.V takes both
-//     (weights exact to about 2^-17, at twice the P.V matrix work). fp8 K/V, whose own
-//     rounding is far coarser, takes the single bf16 pass.
+//     therefore split into hi (p with its low 16 bits cleared, exact) and lo = bf16(p -
+//     hi), and P.V takes both (weights exact to about 2^-16, at twice the P.V matrix
+//     work; l sums p itself). fp8 K/V, whose own rounding is far coarser, takes the
+//     single bf16 pass.
 //   * Tiles wholly at or before the tile's first query position need no mask; the rest
 //     mask positions past each row's own.
 //   * Workgroup ids are dealt so that all query tiles of one (sequence, kv head) land on
@@ -114,9 +115,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr int TQ = ROWS / G;                   // query tokens of the workgroup
   constexpr int NC = D / 32;                     // 32-dim steps of a score MFMA chain
   constexpr int DPL = D / 16;                    // output dims per lane and 16-row group
-  constexpr int CPR = ROWB / 16;                 // 16-byte pool chunks per token row
-  constexpr int CPT = kTileTokens * CPR / kPrefillThreads;  // chunks per thread and tile
-  static_assert(CPT * kPrefillThreads == kTileTokens * CPR, "tile staging layout");
+  constexpr int LB = kBlockTokens * ROWB / kPrefillThreads;  // staged bytes per thread and block
+  constexpr int TPR = ROWB / LB;                 // threads per token row
+  static_assert(LB == 16 || LB == 8 || LB == 4, "one load per thread and block");
+  using LT = typename VChunk<LB>::type;
+  using LT2 = typename VChunk<(LB < 16 ? 2 * LB : 16)>::type;   // fp8 widened to bf16
   static_assert(ROWS % G == 0 && 16 % G == 0, "rows hold whole tokens");
   using VW = typename std::conditional<DPL == 8, u32x4, u32x2>::type;  // DPL 16-bit values
 
@@ -125,12 +128,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 
   // ---- which (sequence, kv head, query tile): id = ((group * tiles) + tile') * 8 + x,
   // pair = group * 8 + x, tile = tiles - 1 - tile'
+  // (integer division runs on the vector ALU: uni() keeps the results scalar)
   const int id = blockIdx.x;
   const int x8 = id & 7, rest = id >> 3;
-  const int pair = (rest / a.num_q_tiles) * 8 + x8;
+  const int grp = uni(rest / a.num_q_tiles);
+  const int pair = grp * 8 + x8;
   if (pair >= a.batch * a.num_kv_heads) return;
-  const int tile = a.num_q_tiles - 1 - rest % a.num_q_tiles;
-  const int b = pair / a.num_kv_heads, kvh = pair - b * a.num_kv_heads;
+  const int tile = a.num_q_tiles - 1 - (rest - grp * a.num_q_tiles);
+  const int b = uni(pair / a.num_kv_heads), kvh = pair - b * a.num_kv_heads;
   // the sequence's rows, kept inside [0, Tq) whatever query_start holds; rows past
   // max_query_len are not computed, though they still count in the positions
   const int Tq = a.num_query_tokens;
@@ -165,75 +170,81 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     const int t = t0 + r / G, h = r % G;
     const bool ok = t < nr;
     qpos[rg] = pos0 + (ok ? t : nr - 1);                   // padding rows copy a real one
+    // padding rows load the last real row (finite scores; never stored)
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
-                          ((size_t)(qs0 + (ok ? t : 0)) * Hq + (size_t)kvh * G + h) * D * 2;
+                          ((size_t)(qs0 + (ok ? t : nr - 1)) * Hq + (size_t)kvh * G + h) * D * 2;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qop[rg][c] = ok ? *reinterpret_cast<const u32x4*>(qrow + (32 * c + 8 * lk) * 2)
-                      : u32x4{0u, 0u, 0u, 0u};
+      qop[rg][c] = *reinterpret_cast<const u32x4*>(qrow + (32 * c + 8 * lk) * 2);
   }
+  // Wait for q here, once: an empty asm that reads and redefines the registers makes the
+  // compiler place that wait now, instead of waiting for every load in flight at the
+  // first use inside the key loop.
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qop[rg][c]));
 
-  // ---- K/V staging: thread tid moves chunks tid + 256 i (token ci / CPR, column ci % CPR)
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  const size_t tok_stride = (size_t)a.num_kv_heads * ROWB;
-  const size_t blk_stride = kBlockTokens * tok_stride;
+  // ---- K/V staging. One load instruction per 16-token block: thread tid moves LB bytes
+  // (16, 8 or 4) at token tid / TPR, byte tid % TPR * LB of the kv head's row, through a
+  // per-block scalar descriptor whose size stops at position L, so later rows read as
+  // zero (stale or NaN slots never meet a p = 0) and missing blocks cost nothing
+  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * ROWB;
+  const size_t blk_stride = (size_t)kBlockTokens * tok_stride;
   const uint8_t* const kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)kvh * ROWB;
   const uint8_t* const vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)kvh * ROWB;
-  // block ids of a tile's 4 blocks (-1 past the sequence); the same for every lane
-  auto load_ids = [&](int kt, int (&ids)[4]) {
+  const uint32_t ld_off = (uint32_t)(tid / TPR) * tok_stride + (uint32_t)(tid % TPR) * LB;
+  // block ids of a tile's 4 blocks: one 16-byte load (table entries j = 4kt .. 4kt+3, the
+  // same for every lane) issued with the K/V prefetch of the tile before, so its wait is
+  // the one the K/V data already takes; entries at or past nb read as 0 and are never used
+  const __amdgpu_buffer_rsrc_t rt =
+      make_rsrc(a.block_tables + (size_t)b * a.max_blocks_per_seq, (uint32_t)nb * 4u);
+  auto load_ids = [&](int kt) -> u32x4 { return buf_load16(rt, (uint32_t)kt * 16u); };
+  auto stage = [&](int kt, const u32x4& idv, LT (&kr)[4], LT (&vr)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = kt * 4 + i;
-      ids[i] = __builtin_amdgcn_readfirstlane(j < nb ? bt[j] : -1);
+      const int rem = L - j * kBlockTokens;             // rows of the block below L
+      const uint32_t pid = (uint32_t)uni((int)idv[i]);
+      const bool ok = rem > 0 && pid < (uint32_t)a.num_blocks;
+      const size_t base = ok ? (size_t)pid * blk_stride : 0;
+      const uint32_t bytes =
+          ok ? (uint32_t)((rem < kBlockTokens ? rem : kBlockTokens) - 1) * tok_stride + ROWB : 0u;
+      kr[i] = VChunk<LB>::load(make_rsrc(kpool + base, bytes), ld_off);
+      vr[i] = VChunk<LB>::load(make_rsrc(vpool + base, bytes), ld_off);
     }
   };
-  // positions at or past L read as zero, so that stale or NaN slots never meet a p = 0
-  auto stage = [&](int kt, const int (&ids)[4], u32x4 (&kr)[CPT], u32x4 (&vr)[CPT]) {
+  auto to_lds = [&](int buf, const LT (&kr)[4], const LT (&vr)[4]) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + kPrefillThreads * i;
-      const int tok = ci / CPR, col = ci % CPR;
-      const int blk = tok / kBlockTokens;
-      const int pid = blk == 0 ? ids[0] : blk == 1 ? ids[1] : blk == 2 ? ids[2] : ids[3];
-      const int pos = kt * kTileTokens + tok;
-      const bool ok = pos < L && (unsigned)pid < (unsigned)a.num_blocks;
-      const size_t off = (size_t)pid * blk_stride + (size_t)(tok % kBlockTokens) * tok_stride +
-                         (size_t)col * 16;
-      kr[i] = vr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (ok) {
-        kr[i] = *reinterpret_cast<const u32x4*>(kpool + off);
-        vr[i] = *reinterpret_cast<const u32x4*>(vpool + off);
-      }
-    }
-  };
-  auto to_lds = [&](int buf, const u32x4 (&kr)[CPT], const u32x4 (&vr)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + kPrefillThreads * i;
-      const int tok = ci / CPR, col = ci % CPR;
+    for (int i = 0; i < 4; ++i) {
+      const int tok = kBlockTokens * i + tid / TPR;
+      const int at = tok * LROW + (tid % TPR) * LB * (KV == PA_FP8_E4M3 ? 2 : 1);
       if constexpr (KV == PA_FP8_E4M3) {
-        // 16 E4M3 values -> 16 bf16 (exact)
-        uint32_t kw[8], vw[8];
+        // LB E4M3 values -> LB bf16 (exact)
+        constexpr int W = LB / 4;
+        uint32_t kw[2 * W], vw[2 * W];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kw[2 * w] = __builtin_bit_cast(uint32_t,
-                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, false));
-          kw[2 * w + 1] = __builtin_bit_cast(uint32_t,
-                                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, true));
-          vw[2 * w] = __builtin_bit_cast(uint32_t,
-                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, false));
-          vw[2 * w + 1] = __builtin_bit_cast(uint32_t,
-                                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, true));
+        for (int w = 0; w < W; ++w) {
+          kw[2 * w] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, false));
+          kw[2 * w + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, true));
+          vw[2 * w] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, false));
+          vw[2 * w + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, true));
         }
-        uint8_t* kd = &s_k[buf][tok * LROW + col * 32];
-        uint8_t* vd = &s_v[buf][tok * LROW + col * 32];
-        *reinterpret_cast<u32x4*>(kd) = u32x4{kw[0], kw[1], kw[2], kw[3]};
-        *reinterpret_cast<u32x4*>(kd + 16) = u32x4{kw[4], kw[5], kw[6], kw[7]};
-        *reinterpret_cast<u32x4*>(vd) = u32x4{vw[0], vw[1], vw[2], vw[3]};
-        *reinterpret_cast<u32x4*>(vd + 16) = u32x4{vw[4], vw[5], vw[6], vw[7]};
+        LT2 kx, vx;
+#pragma unroll
+        for (int w = 0; w < 2 * W; ++w) {
+          kx[w] = kw[w];
+          vx[w] = vw[w];
+        }
+        *reinterpret_cast<LT2*>(&s_k[buf][at]) = kx;
+        *reinterpret_cast<LT2*>(&s_v[buf][at]) = vx;
       } else {
-        *reinterpret_cast<u32x4*>(&s_k[buf][tok * LROW + col * 16]) = kr[i];
-        *reinterpret_cast<u32x4*>(&s_v[buf][tok * LROW + col * 16]) = vr[i];
+        *reinterpret_cast<LT*>(&s_k[buf][at]) = kr[i];
+        *reinterpret_cast<LT*>(&s_v[buf][at]) = vr[i];
       }
     }
   };
@@ -250,7 +261,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     for (int e = 0; e < DPL; ++e) acc[rg][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  auto compute = [&](int buf, int kt) {
+  auto compute = [&](int buf, int kt, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* Kt = s_k[buf];
     const uint8_t* Vt = s_v[buf];
     // scores: sc[rg][s][v] = row li of group rg against token 16s + 4lk + v
@@ -269,7 +281,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         sc[rg][s] = z;
       }
     }
-    const bool masked = kt >= nfull;
     u32x4 aop[RG][2];                      // P as the A operand, two subtiles per MFMA
     u32x4 alo[SPLIT ? RG : 1][2];          // the low parts of P (bf16 K/V)
 #pragma unroll
@@ -281,11 +292,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float x = sc[rg][s][v] * a.qk_scale_log2;
-          if (masked) x = kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] ? x : neg_inf();
+          if constexpr (MASKED)
+            x = kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] ? x : neg_inf();
           sv[s][v] = x;
-          bm = x > bm ? x : bm;
+          bm = fmaxf(bm, x);
         }
-      const float mn = xrow_max(bm > m[rg] ? bm : m[rg]);
+      const float mn = xrow_max(fmaxf(bm, m[rg]));
       const float base = mn == neg_inf() ? 0.0f : mn;
       const float al = m[rg] == mn ? 1.0f : fast_exp2(m[rg] - base);
       float ls = 0.0f;
@@ -298,13 +310,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           for (int v = 0; v < 4; v += 2) {
             const float pa = fast_exp2(sv[2 * pi + h][v] - base);
             const float pb = fast_exp2(sv[2 * pi + h][v + 1] - base);
-            float ra, rb;
-            w[2 * h + v / 2] = pack2<CT>(pa, pb, ra, rb);
             if constexpr (SPLIT) {
+              const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb);
+              w[2 * h + v / 2] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // high halves
               float la, lb;
-              wl[2 * h + v / 2] = pack2<CT>(pa - ra, pb - rb, la, lb);
-              ls += (ra + la) + (rb + lb);
+              wl[2 * h + v / 2] = pack2<CT>(pa - __uint_as_float(ua & 0xffff0000u),
+                                            pb - __uint_as_float(ub & 0xffff0000u), la, lb);
+              ls += pa + pb;
             } else {
+              float ra, rb;
+              w[2 * h + v / 2] = pack2<CT>(pa, pb, ra, rb);
               ls += ra + rb;
             }
           }
@@ -351,23 +366,31 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   };
 
   // ---- the key loop: stage tile kt + 1 (ids one tile further ahead) while computing kt
-  int ids[4];
-  u32x4 kr[CPT], vr[CPT];
+  u32x4 idv = {0u, 0u, 0u, 0u};
+  LT kr[4], vr[4];
   if (ntiles > 0) {
-    load_ids(0, ids);
-    stage(0, ids, kr, vr);
+    idv = load_ids(0);
+    stage(0, idv, kr, vr);
+    idv = load_ids(1);
     to_lds(0, kr, vr);
-    if (ntiles > 1) load_ids(1, ids);
   }
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
+  auto step = [&](int kt, auto masked_tag) {
     const bool more = kt + 1 < ntiles;
-    if (more) stage(kt + 1, ids, kr, vr);
-    if (kt + 2 < ntiles) load_ids(kt + 2, ids);
-    compute(kt & 1, kt);
+    if (more) {
+      stage(kt + 1, idv, kr, vr);
+      idv = load_ids(kt + 2);
+    }
+    compute(kt & 1, kt, masked_tag);
     if (more) to_lds((kt + 1) & 1, kr, vr);
     __syncthreads();
-  }
+  };
+  // tiles wholly at or before the first query position, then the masked rest: two loops,
+  // so that each body is compiled (and its registers allocated) on its own
+  const int nfree = nfull < ntiles ? nfull : ntiles;
+  int kt = 0;
+  for (; kt < nfree; ++kt) step(kt, std::false_type{});
+  for (; kt < ntiles; ++kt) step(kt, std::true_type{});
 
   // ---- normalise and store: lane (j, lk) writes rows 4lk + v, dims DPL*j .. DPL*j+DPL-1
 #pragma unroll
