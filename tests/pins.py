@@ -568,4 +568,178 @@ def pin_prefill_sampled_rows_equal_full():
     assert np.isnan(part[others]).all()
 
 
+# ----------------------------------------------------------------------------- block manager
+
+def _bm(n, bs=16, prefix=True):
+    import oracle.block_manager as obm
+    return obm.BlockManager(n, bs, prefix)
+
+
+def pin_bm_fnv1a64_published_vectors():
+    """FNV-1a 64-bit against the published test vectors of its definition."""
+    import oracle.block_manager as obm
+    assert obm.fnv1a64(b"") == 0xCBF29CE484222325
+    assert obm.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert obm.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def pin_bm_table_example():
+    """The pages' table (logical 0 -> 3, 1 -> 11, 2 -> 7): a sequence that grows through
+    three blocks takes them from the free list in order, and its token positions map to
+    slots through the table (the golden probes)."""
+    g = json.load(open(os.path.join(GOLDEN, "block_table_example.json")))
+    bs, want = g["block_size"], g["table"]
+    m = _bm(g["pool_blocks"], bs, prefix=False)
+    for i in range(g["pool_blocks"]):                 # one block each: sequence i holds block i
+        m.add(i, [i] * bs)
+    for blk in want:                                  # free list becomes 3, 11, 7
+        m.free_seq(blk)
+    m.add(100, [])
+    slots = [m.append(100, 7)[0] for _ in range(41)]
+    assert m.table(100, 3) == want
+    for pos, blk, off in g["probe_tokens"]:
+        assert slots[pos] == blk * bs + off
+
+
+def pin_bm_waste_below_one_block():
+    """The only waste is the unfilled tail of a sequence's last block: fewer than 16 slots,
+    and exactly ceil(L / 16) blocks per sequence, whatever the order of appends."""
+    rng = np.random.default_rng(1)
+    m = _bm(4000)
+    for i in range(40):
+        m.add(i, rng.integers(0, 50000, size=int(rng.integers(0, 300))).tolist())
+    for _ in range(3000):
+        m.append(int(rng.integers(0, 40)), int(rng.integers(0, 50000)))
+    for i in range(40):
+        L, nb = m.seq_len(i), len(m.seqs[i]["blocks"])
+        assert nb == -(-L // 16) and nb * 16 - L < 16
+
+
+def pin_bm_capacity_22048_tokens_640_per_request():
+    """KV space of 22 048 tokens holds about 34 requests of 512 + 128 = 640 tokens (the
+    serving-engine article, section 5): with 16-token blocks, 1378 blocks hold 34 whole
+    requests and the 35th is refused."""
+    import oracle.block_manager as obm
+    m = _bm(22048 // 16, prefix=False)
+    done = 0
+    rng = np.random.default_rng(2)
+    try:
+        while True:
+            m.add(done, rng.integers(0, 50000, size=512).tolist())
+            for _ in range(128):
+                m.append(done, int(rng.integers(0, 50000)))
+            done += 1
+    except obm.NoBlocks:
+        pass
+    assert done == 34 and 22048 // 640 == 34
+
+
+def pin_bm_copy_on_write_parallel_sampling():
+    """N samples share the prompt's blocks (count N); writing into the shared partial last
+    block copies it first, so with 8 samples of a 3000-token prompt the first 7 appends copy
+    and the last writes in place; full prompt blocks are never copied."""
+    m = _bm(400)
+    prompt = list(range(3000))
+    m.add(0, prompt)
+    for c in range(1, 8):
+        m.fork(0, c)
+    shared = list(m.seqs[0]["blocks"])
+    assert len(shared) == 188 and all(m.ref[b] == 8 for b in shared)
+    pairs = []
+    for c in range(8):
+        slot, src, dst = m.append(c, 5)
+        if src >= 0:
+            pairs.append((src, dst))
+            assert slot == dst * 16 + 3000 % 16
+        else:
+            assert slot == shared[-1] * 16 + 3000 % 16
+    assert len(pairs) == 7 and all(src == shared[-1] for src, _ in pairs)
+    assert all(m.ref[b] == 8 for b in shared[:-1]) and m.ref[shared[-1]] == 1
+
+
+def pin_bm_prefix_cache_3000_token_prefix():
+    """A 3000-token shared prefix with 32-token private tails (serving-engine article,
+    section 4): the second request finds the prefix's 187 full blocks (2992 tokens) in the
+    cache, also after the first request has finished (its blocks stay cached)."""
+    rng = np.random.default_rng(3)
+    prefix = rng.integers(0, 50000, size=3000).tolist()
+    m = _bm(1000)
+    assert m.add(0, prefix + rng.integers(0, 50000, size=32).tolist()) == 0
+    assert m.add(1, prefix + rng.integers(0, 50000, size=32).tolist()) == 187 * 16
+    assert m.seqs[1]["blocks"][:187] == m.seqs[0]["blocks"][:187]
+    m.free_seq(0)
+    m.free_seq(1)
+    assert m.add(2, prefix + [1] * 32) == 187 * 16
+
+
+def pin_bm_key_chain_and_salt():
+    """A key stands for the whole prefix: 16 equal tokens after a different first block give
+    a different key (no hit), and the extra data (salt) separates otherwise equal prompts."""
+    m = _bm(100)
+    a = list(range(16)) + list(range(100, 116))
+    b = list(range(1, 17)) + list(range(100, 116))
+    m.add(0, a)
+    assert m.add(1, b) == 0
+    assert m.seqs[0]["keys"][1] != m.seqs[1]["keys"][1]
+    assert m.add(2, a, salt=7) == 0
+    assert m.add(3, a) == 32
+
+
+def pin_bm_only_full_blocks_cached():
+    m = _bm(100)
+    m.add(0, list(range(20)))
+    assert m.stats()[2] == 1
+    assert m.add(1, list(range(20))) == 16
+
+
+def pin_bm_evicts_least_recent_tail_first():
+    """Released cached blocks keep their contents; under pressure the least recently used
+    goes first, and a finished request's blocks enter the queue tail first, so its last
+    block is evicted before its first."""
+    m = _bm(4)
+    m.add(0, list(range(48)))                       # blocks 0, 1, 2 (all full, cached)
+    m.free_seq(0)
+    assert m.evictable == [2, 1, 0] and m.free == [3]
+    m.add(1, [9] * 16)                              # takes free block 3
+    m.add(2, [8] * 16)                              # evicts block 2, the old tail
+    assert m.seqs[2]["blocks"] == [2] and m.evictable == [1, 0]
+    assert m.add(3, list(range(32))) == 32          # blocks 0, 1 still hit
+
+
+def pin_bm_conservation_and_refcounts():
+    """Every block is free, evictable or referenced, and a block's count is the number of
+    tables holding it, through a random stream of adds, forks, appends and releases."""
+    import oracle.block_manager as obm
+    rng = np.random.default_rng(4)
+    m = _bm(300)
+    live, nxt = [], 0
+    shared = rng.integers(0, 1000, size=64).tolist()
+    for _ in range(2000):
+        op = rng.integers(0, 4)
+        try:
+            if op == 0 or not live:
+                m.add(nxt, shared[:int(rng.integers(0, 64))] +
+                      rng.integers(0, 1000, size=int(rng.integers(0, 40))).tolist())
+                live.append(nxt)
+                nxt += 1
+            elif op == 1:
+                m.fork(live[int(rng.integers(0, len(live)))], nxt)
+                live.append(nxt)
+                nxt += 1
+            elif op == 2:
+                m.append(live[int(rng.integers(0, len(live)))], int(rng.integers(0, 1000)))
+            else:
+                m.free_seq(live.pop(int(rng.integers(0, len(live)))))
+        except obm.NoBlocks:
+            pass
+        count = [0] * m.N
+        for s in m.seqs.values():
+            for blk in s["blocks"]:
+                count[blk] += 1
+        assert count == m.ref
+        used = sum(1 for c in count if c > 0)
+        assert len(m.free) + len(m.evictable) + used == m.N
+        assert not set(m.free) & set(m.evictable)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

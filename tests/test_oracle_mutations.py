@@ -10,6 +10,7 @@ import pytest
 import oracle
 import oracle.attention as att
 import oracle.cache_ops as cops
+import oracle.block_manager as obm
 import oracle.prefill as pf
 import oracle.quantize as qz
 import oracle.storage as st
@@ -150,6 +151,56 @@ def _positions_one_early(L, n):
     return np.arange(L - n, L) - 1          # the mask stops one position short
 
 
+def _free_head_first(self, seq_id):
+    s = self.seqs.pop(seq_id)
+    for blk in s["blocks"]:                     # head first instead of tail first
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:
+            (self.evictable if blk in self.block_key else self.free).append(blk)
+
+
+_good_append = obm.BlockManager.append
+
+
+def _append_no_cow(self, seq_id, token):
+    s = self.seqs[seq_id]
+    saved = self.ref[s["blocks"][-1]] if s["blocks"] else None
+    if s["blocks"]:
+        self.ref[s["blocks"][-1]] = 1           # pretend the last block is not shared
+    try:
+        return _good_append(self, seq_id, token)
+    finally:
+        if saved is not None and s["blocks"]:
+            self.ref[s["blocks"][-1]] = max(self.ref[s["blocks"][-1]], saved)
+
+
+_good_key = obm.block_key
+
+
+def _key_unchained(prev, salt, tokens):
+    return _good_key(0, salt, tokens)           # forgets the previous block's key
+
+
+def _append_new_block_each_token(self, seq_id, token):
+    s = self.seqs[seq_id]
+    if self.available() < 1:
+        raise obm.NoBlocks()
+    s["blocks"].append(self._allocate())        # a block per token, full or not
+    s["tokens"].append(token)
+    return s["blocks"][-1] * self.bs, -1, -1
+
+
+def _allocate_evicts_most_recent(self):
+    if self.free:
+        blk = self.free.pop(0)
+    else:
+        blk = self.evictable.pop()              # the most recently released
+        del self.cache[self.block_key.pop(blk)]
+        del self.block_tokens[blk]
+    self.ref[blk] = 1
+    return blk
+
+
 MUTATIONS = {
     "gqa_interleaved": (att, "kv_head_of", _interleaved_gqa),
     "no_length_mask": (att, "gather_sequence", _no_truncation),
@@ -168,6 +219,11 @@ MUTATIONS = {
     "prefill_positions_from_start": (pf, "query_positions", _positions_from_start),
     "prefill_no_causal_mask": (pf, "prefill_ref", _prefill_no_causal_mask),
     "prefill_mask_one_short": (pf, "query_positions", _positions_one_early),
+    "bm_release_head_first": (obm.BlockManager, "free_seq", _free_head_first),
+    "bm_no_copy_on_write": (obm.BlockManager, "append", _append_no_cow),
+    "bm_key_unchained": (obm, "block_key", _key_unchained),
+    "bm_block_per_token": (obm.BlockManager, "append", _append_new_block_each_token),
+    "bm_evicts_most_recent": (obm.BlockManager, "_allocate", _allocate_evicts_most_recent),
 }
 
 
