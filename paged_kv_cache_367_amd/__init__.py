@@ -12,3 +12,4 @@ from .binding import (  # noqa: F401
     pa_abi_version, pa_status_string, pa_decode_max_chunks, decode_workspace, pa_decode_workspace_bytes,
     pa_decode, pa_prefill, pa_cache_write, pa_cache_write_fp8, pa_block_copy,
 )
+from .block_manager import BlockManager, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ  # noqa: F401

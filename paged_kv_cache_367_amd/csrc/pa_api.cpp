@@ -125,6 +125,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PA_ERR_HIP: return "HIP runtime error at launch";
+    case -8: return "not enough free or evictable KV blocks";      // pa_block_manager.h
+    case -9: return "unknown sequence id, or the id is in use";   // pa_block_manager.h
     default: return "unknown status";
   }
 }
