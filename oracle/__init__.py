@@ -13,8 +13,10 @@ Everything is plain numpy in float64:
   attention    decode_ref: gather each sequence's blocks through its block table into
                a contiguous array, truncate to the context length, and apply textbook
                softmax attention per query head (GQA kv head = h // group).
-  cache_ops    cache_write_ref (slot write of new tokens) and block_copy_ref
-               (copy-on-write block copy), both bit copies.
+  cache_ops    cache_write_ref (slot write of new tokens), block_copy_ref (copy-on-write
+               block copy) and block_swap_ref (blocks between two pools), bit copies.
+  block_manager  BlockManager: free list, reference counts, copy-on-write, prefix-cache
+               key chain, LRU eviction and swapping to a host pool (host bookkeeping).
   prefill      prefill_ref: n new query tokens per sequence attending causally over
                the paged cache (chunked prefill, prefix-cache tail prefill).
   quantize     e4m3_encode and cache_write_fp8_ref: the slot write into an fp8 E4M3
@@ -26,7 +28,7 @@ print, closed forms, library routines and brute force.
 """
 from .storage import decode_storage, e4m3_table, bf16_bits_to_f64
 from .attention import decode_ref, attend, gather_sequence, kv_head_of
-from .cache_ops import cache_write_ref, block_copy_ref
+from .cache_ops import cache_write_ref, block_copy_ref, block_swap_ref
 from .quantize import e4m3_encode, quant_inputs, cache_write_fp8_ref
 from .prefill import prefill_ref, query_positions
 from .formulas import kv_bytes_per_token, kv_bytes_per_request
@@ -34,7 +36,7 @@ from .formulas import kv_bytes_per_token, kv_bytes_per_request
 __all__ = [
     "decode_storage", "e4m3_table", "bf16_bits_to_f64",
     "decode_ref", "attend", "gather_sequence", "kv_head_of",
-    "cache_write_ref", "block_copy_ref",
+    "cache_write_ref", "block_copy_ref", "block_swap_ref",
     "e4m3_encode", "quant_inputs", "cache_write_fp8_ref",
     "prefill_ref", "query_positions",
     "kv_bytes_per_token", "kv_bytes_per_request",

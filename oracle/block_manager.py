@@ -26,6 +26,12 @@ Readings where the pages leave the policy open (the same as the C ABI states):
   - release walks a sequence's blocks from the last to the first; a count reaching zero
     sends a cached block to the evictable queue's tail, any other to the free list's tail;
     a cache hit takes the block out of the queue.
+  - preemption by swapping (vLLM-PagedAttention与连续批处理技术拆解, section 4.3: a victim's
+    KV moves to CPU memory and comes back later): a host pool with its own first-in
+    first-out free list; swap-out gives every block of an unshared sequence a host block in
+    order and releases the device blocks as a finished sequence's are; swap-in allocates
+    fresh device blocks, returns the host blocks to the tail of the host free list and
+    registers the full blocks' keys when free.
 """
 from __future__ import annotations
 
@@ -63,7 +69,8 @@ class BlockManager:
         self.cache = {}                         # key -> block
         self.block_key = {}                     # cached block -> key
         self.block_tokens = {}                  # cached block -> its token ids
-        self.seqs = {}                          # id -> dict(blocks, tokens, keys, salt)
+        self.seqs = {}                          # id -> dict(blocks, tokens, keys, salt, swapped)
+        self.host_free = None                   # host pool free list, once configured
 
     # -- helpers
     def available(self) -> int:
@@ -122,12 +129,15 @@ class BlockManager:
             blocks.append(blk)
             if j < nfull:
                 self._register(blk, keys[j], tokens[j * bs:(j + 1) * bs])
-        self.seqs[seq_id] = dict(blocks=blocks, tokens=list(tokens), keys=keys, salt=salt)
+        self.seqs[seq_id] = dict(blocks=blocks, tokens=list(tokens), keys=keys, salt=salt,
+                                 swapped=False)
         return len(hits) * bs
 
     def append(self, seq_id, token):
         """Returns (slot, cow_src, cow_dst); the pair is (-1, -1) without a copy."""
         s = self.seqs[seq_id]
+        if s["swapped"]:
+            raise ValueError("sequence is swapped out")
         bs = self.bs
         off = len(s["tokens"]) % bs
         src = dst = -1
@@ -157,17 +167,61 @@ class BlockManager:
         if child in self.seqs:
             raise KeyError(child)
         p = self.seqs[parent]
+        if p["swapped"]:
+            raise ValueError("sequence is swapped out")
         for blk in p["blocks"]:
             self.ref[blk] += 1
         self.seqs[child] = dict(blocks=list(p["blocks"]), tokens=list(p["tokens"]),
-                                keys=list(p["keys"]), salt=p["salt"])
+                                keys=list(p["keys"]), salt=p["salt"], swapped=False)
 
     def free_seq(self, seq_id):
         s = self.seqs.pop(seq_id)
+        if s["swapped"]:
+            self.host_free.extend(s["blocks"])
+            return
         for blk in reversed(s["blocks"]):
             self.ref[blk] -= 1
             if self.ref[blk] == 0:
                 (self.evictable if blk in self.block_key else self.free).append(blk)
+
+    def set_host_blocks(self, n):
+        if self.host_free is not None or n < 1:
+            raise ValueError("host pool already set or empty")
+        self.host_free = list(range(n))
+
+    def swap_out(self, seq_id):
+        """Returns the (device block, host block) pairs."""
+        s = self.seqs[seq_id]
+        if s["swapped"] or any(self.ref[b] > 1 for b in s["blocks"]):
+            raise ValueError("cannot swap out")
+        if len(self.host_free) < len(s["blocks"]):
+            raise NoBlocks()
+        host = [self.host_free.pop(0) for _ in s["blocks"]]
+        pairs = list(zip(s["blocks"], host))
+        for blk in reversed(s["blocks"]):
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                (self.evictable if blk in self.block_key else self.free).append(blk)
+        s["blocks"], s["swapped"] = host, True
+        return pairs
+
+    def swap_in(self, seq_id):
+        """Returns the (host block, device block) pairs."""
+        s = self.seqs[seq_id]
+        if not s["swapped"]:
+            raise ValueError("not swapped out")
+        if self.available() < len(s["blocks"]):
+            raise NoBlocks()
+        dev = []
+        for j, h in enumerate(s["blocks"]):
+            blk = self._allocate()
+            dev.append(blk)
+            if j < len(s["keys"]):
+                self._register(blk, s["keys"][j], s["tokens"][j * self.bs:(j + 1) * self.bs])
+        pairs = list(zip(s["blocks"], dev))
+        self.host_free.extend(s["blocks"])
+        s["blocks"], s["swapped"] = dev, False
+        return pairs
 
     # -- queries
     def slots(self, seq_id, first, count):

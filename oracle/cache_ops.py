@@ -37,3 +37,17 @@ def block_copy_ref(pool: np.ndarray, pairs: np.ndarray) -> np.ndarray:
     for s, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         ob[d] = src_state[s]
     return out
+
+
+def block_swap_ref(dst_pool: np.ndarray, src_pool: np.ndarray, pairs: np.ndarray) -> np.ndarray:
+    """Whole blocks from one pool to another (swap-out to host memory, swap-in back):
+    returns a copy of dst_pool with dst_pool[d] = src_pool[s] for every (s, d) in pairs
+    (vLLM-PagedAttention与连续批处理技术拆解, section 4.3, preemption by swapping). Pairs with
+    an id outside either pool are skipped."""
+    if dst_pool.shape[1:] != src_pool.shape[1:]:
+        raise ValueError("pools differ in block shape")
+    out = np.array(dst_pool, copy=True)
+    for s, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= s < src_pool.shape[0] and 0 <= d < dst_pool.shape[0]:
+            out[d] = src_pool[s]
+    return out

@@ -742,4 +742,55 @@ def pin_bm_conservation_and_refcounts():
         assert not set(m.free) & set(m.evictable)
 
 
+def pin_block_swap_round_trip():
+    """Swapping blocks to a second pool and back restores them bit for bit; blocks not named
+    stay as they were; pairs outside either pool are skipped."""
+    rng = np.random.default_rng(5)
+    dev = rng.integers(0, 1 << 16, size=(12, 16, 2, 8), dtype=np.uint16)
+    host = np.zeros((6, 16, 2, 8), dtype=np.uint16)
+    out_pairs = np.array([[3, 0], [7, 1], [11, 5], [12, 2], [2, 6]])   # last two skipped
+    host2 = oracle.block_swap_ref(host, dev, out_pairs)
+    assert np.array_equal(host2[[0, 1, 5]], dev[[3, 7, 11]])
+    assert not host2[[2, 3, 4]].any()
+    blank = np.zeros_like(dev)
+    back = oracle.block_swap_ref(blank, host2, np.array([[0, 9], [1, 4], [5, 0]]))
+    assert np.array_equal(back[[9, 4, 0]], dev[[3, 7, 11]])
+    assert not np.delete(back, [9, 4, 0], axis=0).any()
+
+
+def pin_bm_swap_preemption_keeps_contents():
+    """Preemption by swapping: a victim's blocks go to host memory, its device blocks serve
+    another sequence, and after swap-in every token of the victim reads the K/V it had
+    (pools simulated with one label per slot, moved with the oracle's block swap)."""
+    m = _bm(12, bs=4, prefix=False)
+    m.set_host_blocks(10)
+    dev = np.full((12, 4), -1, dtype=np.int64)
+    host = np.full((10, 4), -1, dtype=np.int64)
+
+    def write(seq, first, n, base):
+        for i, slot in enumerate(m.slots(seq, first, n)):
+            dev[slot // 4, slot % 4] = base + first + i
+
+    m.add(7, list(range(12)))                      # device blocks 0-2, stays resident
+    m.add(8, [1])                                  # device block 3, swapped out to host 0
+    m.swap_out(8)
+    m.add(0, list(range(17)))                      # device blocks 4-8
+    write(0, 0, 17, 1000)
+    before = [dev[sl // 4, sl % 4] for sl in m.slots(0, 0, 17)]
+    pairs = m.swap_out(0)                          # to host blocks 1-5
+    assert [tuple(p) for p in pairs] == [(4, 1), (5, 2), (6, 3), (7, 4), (8, 5)]
+    host = oracle.block_swap_ref(host[:, :, None, None], dev[:, :, None, None],
+                                 np.array(pairs))[:, :, 0, 0]
+    assert m.stats()[0] == 9                       # its device blocks are free again
+    m.add(1, list(range(100, 136)))                # a second sequence takes all 9 of them
+    write(1, 0, 36, 5000)
+    m.free_seq(1)
+    back = m.swap_in(0)
+    dev = oracle.block_swap_ref(dev[:, :, None, None], host[:, :, None, None],
+                                np.array(back))[:, :, 0, 0]
+    assert [dev[sl // 4, sl % 4] for sl in m.slots(0, 0, 17)] == before
+    slot, _, _ = m.append(0, 3)
+    assert slot // 4 == m.table(0, 5)[4]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -201,6 +201,21 @@ def _allocate_evicts_most_recent(self):
     return blk
 
 
+def _swap_reversed(dst_pool, src_pool, pairs):
+    out = np.array(dst_pool, copy=True)
+    for s_, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= d < src_pool.shape[0] and 0 <= s_ < dst_pool.shape[0]:
+            out[s_] = src_pool[d]                   # pair read as (dst, src)
+    return out
+
+
+_good_swap_out = obm.BlockManager.swap_out
+
+
+def _swap_out_pairs_reversed(self, seq_id):
+    return [(h, d) for d, h in _good_swap_out(self, seq_id)]
+
+
 MUTATIONS = {
     "gqa_interleaved": (att, "kv_head_of", _interleaved_gqa),
     "no_length_mask": (att, "gather_sequence", _no_truncation),
@@ -224,6 +239,8 @@ MUTATIONS = {
     "bm_key_unchained": (obm, "block_key", _key_unchained),
     "bm_block_per_token": (obm.BlockManager, "append", _append_new_block_each_token),
     "bm_evicts_most_recent": (obm.BlockManager, "_allocate", _allocate_evicts_most_recent),
+    "swap_pair_reversed": (cops, "block_swap_ref", _swap_reversed),
+    "bm_swap_out_pairs_reversed": (obm.BlockManager, "swap_out", _swap_out_pairs_reversed),
 }
 
 
