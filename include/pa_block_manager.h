@@ -116,6 +116,31 @@ int32_t pa_bm_stats(const pa_block_manager_t* bm, int32_t* num_free, int32_t* nu
 /* Physical blocks in eviction order (head first) into out[cap]; returns the count. */
 int32_t pa_bm_evictable(const pa_block_manager_t* bm, int32_t* out, int32_t cap);
 
+/* Preemption by swapping (vLLM-PagedAttention与连续批处理技术拆解, section 4.3): a victim's
+ * blocks move to host memory and come back when device blocks are free again. The host pool
+ * has host_blocks blocks with its own FIFO free list (0 .. host_blocks-1); call this once,
+ * before any swap (PA_ERR_SHAPE if called twice or host_blocks < 1). */
+int32_t pa_bm_set_host_blocks(pa_block_manager_t* bm, int32_t host_blocks);
+
+/* Swap seq_id out: every block gets a host block (in order, from the host free list), the
+ * (device block, host block) pairs go to pairs[2 * nb] for pa_block_swap(host pool <- device
+ * pool), and the device blocks are released as pa_bm_free releases them (a cached block stays
+ * findable until evicted). The sequence keeps its tokens and keys but has no device blocks
+ * until swapped in; append and fork fail on it (PA_ERR_UNSUPPORTED), as does swapping out a
+ * sequence with a shared block (count > 1): sharing sequences are preempted together by
+ * recomputation instead. Returns nb, PA_ERR_NO_BLOCKS if the host pool is short, or
+ * PA_ERR_SHAPE if cap < nb. */
+int32_t pa_bm_swap_out(pa_block_manager_t* bm, int64_t seq_id, int64_t* pairs, int32_t cap);
+
+/* Swap seq_id back in: fresh device blocks (allocated as usual), the (host block, device
+ * block) pairs into pairs[2 * nb] for pa_block_swap(device pool <- host pool), host blocks
+ * back to the tail of the host free list, and full blocks registered in the prefix cache
+ * under their keys when those are free. Returns nb or an error (nothing changed). */
+int32_t pa_bm_swap_in(pa_block_manager_t* bm, int64_t seq_id, int64_t* pairs, int32_t cap);
+
+/* Blocks on the host free list. */
+int32_t pa_bm_host_free(const pa_block_manager_t* bm);
+
 #ifdef __cplusplus
 }
 #endif

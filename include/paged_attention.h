@@ -245,6 +245,21 @@ pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pai
                           int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
                           void* stream);
 
+/* Block swap between two pools (preemption by swapping: a victim sequence's blocks move to
+ * host memory and come back later; vLLM-PagedAttention与连续批处理技术拆解, section 4.3). For
+ * each pair p: dst_k_pool[dst_p] = src_k_pool[src_p] and dst_v_pool[dst_p] =
+ * src_v_pool[src_p], whole blocks (block_size x Hkv x d), bit-exact, one launch for all
+ * pairs. Either pool may be device memory or pinned host memory (hipHostMalloc); the pairs
+ * [P, 2] int64 (src block in the source pool, dst block in the destination pool) must be
+ * device-accessible (device memory or pinned host memory). The pools must not overlap and
+ * destinations must be distinct; pairs with an id outside [0, src_num_blocks) or
+ * [0, dst_num_blocks) are skipped. Sizes as for pa_block_copy (num_blocks there is
+ * dst_num_blocks here); P * 64 < 2^31. */
+pa_status_t pa_block_swap(void* dst_k_pool, void* dst_v_pool, int32_t dst_num_blocks,
+                          const void* src_k_pool, const void* src_v_pool, int32_t src_num_blocks,
+                          const int64_t* src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t kv_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

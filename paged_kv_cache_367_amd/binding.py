@@ -66,6 +66,8 @@ def load_library():
     lib.pa_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P]
     lib.pa_cache_write_fp8.restype = I32
     lib.pa_cache_write_fp8.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, F, P]
+    lib.pa_block_swap.restype = I32
+    lib.pa_block_swap.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, I32, I32, P]
     lib.pa_block_copy.restype = I32
     lib.pa_block_copy.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P]
     _LIB = lib
@@ -258,3 +260,36 @@ def pa_block_copy(k_pool, v_pool, src_dst_pairs, stream=None):
                            _stream(stream))
     if st != 0:
         raise PaError(st, "pa_block_copy")
+
+
+def _any_mem(t, name):
+    """Pointer of a contiguous tensor on the GPU or in pinned host memory."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pa_block_swap(dst_k, dst_v, src_k, src_v, src_dst_pairs, stream=None):
+    """Copy whole blocks src -> dst between two pools (either may be pinned host memory);
+    pairs int64 [P, 2] on the GPU or pinned."""
+    import torch
+    lib = load_library()
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_k.dtype != src_k.dtype:
+        raise ValueError("the pools differ in block shape or dtype")
+    if dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("K and V pools differ in shape")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2 or \
+            src_dst_pairs.dtype != torch.int64:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    N, bs, Hkv, d = dst_k.shape
+    st = lib.pa_block_swap(_any_mem(dst_k, "dst_k"), _any_mem(dst_v, "dst_v"), N,
+                           _any_mem(src_k, "src_k"), _any_mem(src_v, "src_v"), src_k.shape[0],
+                           _any_mem(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0],
+                           Hkv, d, bs, dtype_code(dst_k), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_block_swap")

@@ -52,6 +52,14 @@ def _lib():
         lib.pa_bm_stats.argtypes = [P, pi32, pi32, pi32]
         lib.pa_bm_evictable.restype = I32
         lib.pa_bm_evictable.argtypes = [P, pi32, I32]
+        lib.pa_bm_set_host_blocks.restype = I32
+        lib.pa_bm_set_host_blocks.argtypes = [P, I32]
+        lib.pa_bm_swap_out.restype = I32
+        lib.pa_bm_swap_out.argtypes = [P, I64, pi64, I32]
+        lib.pa_bm_swap_in.restype = I32
+        lib.pa_bm_swap_in.argtypes = [P, I64, pi64, I32]
+        lib.pa_bm_host_free.restype = I32
+        lib.pa_bm_host_free.argtypes = [P]
         _READY = True
     return lib
 
@@ -151,3 +159,23 @@ class BlockManager:
         out = np.empty(self.num_blocks, dtype=np.int32)
         n = _check(self._lib.pa_bm_evictable(self._h, _i32p(out), out.size), "pa_bm_evictable")
         return out[:n].tolist()
+
+    def set_host_blocks(self, n: int):
+        _check(self._lib.pa_bm_set_host_blocks(self._h, int(n)), "pa_bm_set_host_blocks")
+
+    def _swap(self, fn, seq_id, where):
+        cap = self.num_blocks
+        pairs = np.empty((cap, 2), dtype=np.int64)
+        n = _check(fn(self._h, int(seq_id), _i64p(pairs), cap), where)
+        return pairs[:n].copy()
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """(device block, host block) pairs int64 [nb, 2] for pa_block_swap."""
+        return self._swap(self._lib.pa_bm_swap_out, seq_id, "pa_bm_swap_out")
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """(host block, device block) pairs int64 [nb, 2] for pa_block_swap."""
+        return self._swap(self._lib.pa_bm_swap_in, seq_id, "pa_bm_swap_in")
+
+    def host_free(self) -> int:
+        return _check(self._lib.pa_bm_host_free(self._h), "pa_bm_host_free")

@@ -352,4 +352,27 @@ pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pai
   return PA_OK;
 }
 
+pa_status_t pa_block_swap(void* dst_k_pool, void* dst_v_pool, int32_t dst_num_blocks,
+                          const void* src_k_pool, const void* src_v_pool, int32_t src_num_blocks,
+                          const int64_t* src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t kv_dtype, void* stream) {
+  int64_t row_bytes = 0;
+  if (num_pairs < 0 || src_num_blocks <= 0) return PA_ERR_SHAPE;
+  pa_status_t st = check_cache_args(num_kv_heads, head_dim, block_size, dst_num_blocks, kv_dtype,
+                                    &row_bytes);
+  if (st != PA_OK) return st;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k_pool || !dst_v_pool || !src_k_pool || !src_v_pool || !src_dst_pairs)
+    return PA_ERR_NULL;
+  if (!aligned(dst_k_pool, 16) || !aligned(dst_v_pool, 16) || !aligned(src_k_pool, 16) ||
+      !aligned(src_v_pool, 16) || !aligned(src_dst_pairs, 8))
+    return PA_ERR_ALIGN;
+  if ((int64_t)num_pairs * 64 > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (pa::launch_block_swap(dst_k_pool, dst_v_pool, dst_num_blocks, src_k_pool, src_v_pool,
+                            src_num_blocks, src_dst_pairs, num_pairs, row_bytes * block_size,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
 }  // extern "C"

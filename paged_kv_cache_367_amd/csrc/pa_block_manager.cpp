@@ -41,10 +41,11 @@ uint64_t block_key(uint64_t prev, uint64_t salt, const int32_t* tok, int n) {
 }
 
 struct Seq {
-  std::vector<int32_t> blocks;
+  std::vector<int32_t> blocks;   // device blocks, or host blocks while swapped out
   std::vector<int32_t> tokens;
-  std::vector<uint64_t> keys;   // one per full block
+  std::vector<uint64_t> keys;    // one per full block
   uint64_t salt = 0;
+  bool swapped = false;
 };
 
 }  // namespace
@@ -62,6 +63,8 @@ struct pa_block_manager {
   int32_t q_head = -1, q_tail = -1, q_len = 0;
   std::unordered_map<uint64_t, int32_t> map;
   std::unordered_map<int64_t, Seq> seqs;
+  int32_t host_blocks = 0;
+  std::deque<int32_t> host_free;
 
   pa_block_manager(int32_t n, int32_t b, bool p)
       : N(n), bs(b), prefix(p), ref(n, 0), cached(n, 0), key(n, 0), btok((size_t)n * b, 0),
@@ -185,6 +188,7 @@ int32_t pa_bm_append(pa_block_manager_t* bm, int64_t seq_id, int32_t token, int6
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   Seq& s = it->second;
+  if (s.swapped) return PA_ERR_UNSUPPORTED;
   const int32_t bs = bm->bs;
   const int32_t len = (int32_t)s.tokens.size(), off = len % bs;
   int64_t src = -1, dst = -1;
@@ -219,6 +223,7 @@ int32_t pa_bm_fork(pa_block_manager_t* bm, int64_t parent_id, int64_t child_id) 
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(parent_id);
   if (it == bm->seqs.end() || bm->seqs.count(child_id)) return PA_ERR_UNKNOWN_SEQ;
+  if (it->second.swapped) return PA_ERR_UNSUPPORTED;
   Seq child = it->second;
   for (int32_t blk : child.blocks) ++bm->ref[blk];
   bm->seqs.emplace(child_id, std::move(child));
@@ -230,7 +235,11 @@ int32_t pa_bm_free(pa_block_manager_t* bm, int64_t seq_id) {
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   const std::vector<int32_t>& b = it->second.blocks;
-  for (size_t i = b.size(); i-- > 0;) bm->release(b[i]);   // tail first
+  if (it->second.swapped) {
+    for (int32_t h : b) bm->host_free.push_back(h);
+  } else {
+    for (size_t i = b.size(); i-- > 0;) bm->release(b[i]);   // tail first
+  }
   bm->seqs.erase(it);
   return PA_OK;
 }
@@ -241,6 +250,7 @@ int32_t pa_bm_slots(const pa_block_manager_t* bm, int64_t seq_id, int32_t first,
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   const Seq& s = it->second;
+  if (s.swapped) return PA_ERR_UNSUPPORTED;
   if (first < 0 || count < 0 || (int64_t)first + count > (int64_t)s.tokens.size())
     return PA_ERR_SHAPE;
   if (count > 0 && !slots) return PA_ERR_NULL;
@@ -256,6 +266,7 @@ int32_t pa_bm_block_table(const pa_block_manager_t* bm, int64_t seq_id, int32_t*
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  if (it->second.swapped) return PA_ERR_UNSUPPORTED;
   const std::vector<int32_t>& b = it->second.blocks;
   if (width < (int32_t)b.size()) return PA_ERR_SHAPE;
   if (width > 0 && !row) return PA_ERR_NULL;
@@ -271,6 +282,7 @@ int32_t pa_bm_tables(const pa_block_manager_t* bm, const int64_t* seq_ids, int32
   for (int32_t i = 0; i < n; ++i) {          // check everything before writing anything
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PA_ERR_UNSUPPORTED;
     if ((int32_t)it->second.blocks.size() > width) return PA_ERR_SHAPE;
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -320,6 +332,68 @@ int32_t pa_bm_evictable(const pa_block_manager_t* bm, int32_t* out, int32_t cap)
   int32_t n = 0;
   for (int32_t b = bm->q_head; b >= 0 && n < cap; b = bm->next[b]) out[n++] = b;
   return n;
+}
+
+int32_t pa_bm_set_host_blocks(pa_block_manager_t* bm, int32_t host_blocks) {
+  if (!bm) return PA_ERR_NULL;
+  if (host_blocks < 1 || host_blocks > (1 << 30) || bm->host_blocks > 0) return PA_ERR_SHAPE;
+  bm->host_blocks = host_blocks;
+  for (int32_t i = 0; i < host_blocks; ++i) bm->host_free.push_back(i);
+  return PA_OK;
+}
+
+int32_t pa_bm_swap_out(pa_block_manager_t* bm, int64_t seq_id, int64_t* pairs, int32_t cap) {
+  if (!bm) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  Seq& s = it->second;
+  const int32_t nb = (int32_t)s.blocks.size();
+  if (s.swapped) return PA_ERR_UNSUPPORTED;
+  for (int32_t blk : s.blocks)
+    if (bm->ref[blk] > 1) return PA_ERR_UNSUPPORTED;
+  if (cap < nb) return PA_ERR_SHAPE;
+  if (nb > 0 && !pairs) return PA_ERR_NULL;
+  if ((int32_t)bm->host_free.size() < nb) return PA_ERR_NO_BLOCKS;
+  std::vector<int32_t> host(nb);
+  for (int32_t j = 0; j < nb; ++j) {
+    host[j] = bm->host_free.front();
+    bm->host_free.pop_front();
+    pairs[2 * j] = s.blocks[j];
+    pairs[2 * j + 1] = host[j];
+  }
+  for (int32_t j = nb; j-- > 0;) bm->release(s.blocks[j]);    // tail first, as pa_bm_free
+  s.blocks = std::move(host);
+  s.swapped = true;
+  return nb;
+}
+
+int32_t pa_bm_swap_in(pa_block_manager_t* bm, int64_t seq_id, int64_t* pairs, int32_t cap) {
+  if (!bm) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  Seq& s = it->second;
+  const int32_t nb = (int32_t)s.blocks.size();
+  if (!s.swapped) return PA_ERR_UNSUPPORTED;
+  if (cap < nb) return PA_ERR_SHAPE;
+  if (nb > 0 && !pairs) return PA_ERR_NULL;
+  if (bm->available() < nb) return PA_ERR_NO_BLOCKS;
+  std::vector<int32_t> dev(nb);
+  for (int32_t j = 0; j < nb; ++j) {
+    dev[j] = bm->allocate();
+    pairs[2 * j] = s.blocks[j];
+    pairs[2 * j + 1] = dev[j];
+    if (j < (int32_t)s.keys.size())
+      bm->register_full(dev[j], s.keys[j], s.tokens.data() + (size_t)j * bm->bs);
+  }
+  for (int32_t h : s.blocks) bm->host_free.push_back(h);
+  s.blocks = std::move(dev);
+  s.swapped = false;
+  return nb;
+}
+
+int32_t pa_bm_host_free(const pa_block_manager_t* bm) {
+  if (!bm) return PA_ERR_NULL;
+  return (int32_t)bm->host_free.size();
 }
 
 }  // extern "C"

@@ -168,6 +168,26 @@ hipError_t launch_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new,
   return hipGetLastError();
 }
 
+// Whole blocks from one pool to another, K and V; either pool may be pinned host memory
+// (swap-out and swap-in of preempted sequences). Workgroup w copies 4 KB pieces of pair
+// w / gx (so the pair is read once per wave, as a uniform load), 16 bytes per thread.
+__global__ __launch_bounds__(256) void block_swap_kernel(
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, int32_t dst_blocks,
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v, int32_t src_blocks,
+    const int64_t* __restrict__ pairs, int64_t block_chunks, int32_t gx) {
+  const int p = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (uint32_t)gx));
+  const int part = (int)blockIdx.x - p * gx;
+  const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  for (int64_t c = (int64_t)part * 256 + threadIdx.x; c < block_chunks; c += (int64_t)gx * 256) {
+    const int64_t so = (src * block_chunks + c) * 16, d_o = (dst * block_chunks + c) * 16;
+    const u32x4 k = *reinterpret_cast<const u32x4*>(src_k + so);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src_v + so);
+    *reinterpret_cast<u32x4*>(dst_k + d_o) = k;
+    *reinterpret_cast<u32x4*>(dst_v + d_o) = v;
+  }
+}
+
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int64_t* pairs,
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream) {
@@ -177,6 +197,19 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int64_t* pairs,
   block_copy_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), pairs, num_pairs,
       block_chunks, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_swap(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k,
+                             const void* src_v, int32_t src_blocks, const int64_t* pairs,
+                             int32_t num_pairs, int64_t block_bytes, hipStream_t stream) {
+  const int64_t block_chunks = block_bytes / 16;
+  const int64_t per_pair = (block_chunks + 255) / 256;
+  const int32_t gx = (int32_t)(per_pair < 64 ? per_pair : 64);
+  block_swap_kernel<<<dim3((uint32_t)((int64_t)num_pairs * gx)), dim3(256), 0, stream>>>(
+      static_cast<uint8_t*>(dst_k), static_cast<uint8_t*>(dst_v), dst_blocks,
+      static_cast<const uint8_t*>(src_k), static_cast<const uint8_t*>(src_v), src_blocks, pairs,
+      block_chunks, gx);
   return hipGetLastError();
 }
 

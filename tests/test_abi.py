@@ -176,3 +176,21 @@ def test_prefill_rejects_before_launch(lib):
     assert _prefill(lib, _pdesc(), scale=float("inf")) == -2
     assert _prefill(lib, _pdesc(batch=0)) == 0                      # nothing to do
     assert _prefill(lib, _pdesc(), max_q=0) == 0
+
+
+def test_block_swap_rejects_before_launch(lib):
+    p = ctypes.c_void_p(0x10000)
+    z = ctypes.c_void_p(0)
+    sw = lambda *a: lib.pa_block_swap(*a)                          # noqa: E731
+    # dst_k, dst_v, dst_N, src_k, src_v, src_N, pairs, P, Hkv, d, bs, dtype, stream
+    assert sw(p, p, 10, p, p, 10, p, -1, 8, 128, 16, pa.PA_BF16, None) == -2
+    assert sw(p, p, 10, p, p, 0, p, 1, 8, 128, 16, pa.PA_BF16, None) == -2
+    assert sw(p, p, 0, p, p, 10, p, 1, 8, 128, 16, pa.PA_BF16, None) == -2
+    assert sw(p, p, 10, p, p, 10, p, 0, 8, 128, 16, pa.PA_BF16, None) == 0
+    assert sw(p, p, 10, z, p, 10, p, 1, 8, 128, 16, pa.PA_BF16, None) == -1
+    assert sw(p, p, 10, p, p, 10, z, 1, 8, 128, 16, pa.PA_BF16, None) == -1
+    assert sw(p, p, 10, p, p, 10, p, 1, 8, 128, 16, 11, None) == -3
+    assert sw(p, ctypes.c_void_p(0x10008), 10, p, p, 10, p, 1, 8, 128, 16, pa.PA_BF16,
+              None) == -6
+    assert sw(p, p, 10, p, p, 10, ctypes.c_void_p(0x10004), 1, 8, 128, 16, pa.PA_BF16,
+              None) == -6
