@@ -21,7 +21,17 @@ K/V, then causal multi-token attention (pa_prefill). Its value is attention TFLO
 counting only the unmasked work, 4 * d * Hq flops per (query token, attended position),
 and its roofline is the bf16 matrix-core peak.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3] [--path decode|prefill]
+With --path swap the step is a preemption by swapping: 16 384 Llama-3-8B-shaped blocks
+(8 kv heads, d=128, bf16: 64 KiB of K and V each, 1 GiB in all) move from the device pool
+to a pinned host pool with pa_block_swap and back; value is GB/s per direction against the
+host link (PCIe 5.0 x16, 64 GB/s per direction). With --path manager the step is the host
+bookkeeping of one decode step of the Llama-3-8B workload (256 sequences, lognormal
+lengths): one appended token per sequence (one pa_bm_append_batch call) plus the export of
+the block tables (one pa_bm_tables call); value is steps per second, the oracle's Python
+manager as baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3]
+                       [--path decode|prefill|swap|manager]
 """
 from __future__ import annotations
 
@@ -42,7 +52,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published peak
 PREFILL_METRIC = "paged-attn chunked-prefill attention TFLOP/s (causal, algorithmic), 8B GQA bf16 layer"
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_367_amd", "csrc", "pa_decode.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_367_amd", "csrc", f)
+                  for f in ("pa_decode.hip", "pa_device.h")]
 
 
 def log(msg):
@@ -50,7 +61,11 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the decode kernel's sources, concatenated."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(config_name: str):
@@ -248,6 +263,124 @@ def run_prefill(args) -> int:
     return 0
 
 
+PCIE_PEAK_GBS = 64.0        # PCIe 5.0 x16 host link, per direction
+
+
+def run_swap(args) -> int:
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_367_amd as pa
+
+    nblk, Hkv, d = 16384, 8, 128
+    Nd = nblk + 1024
+    rng = np.random.default_rng(367)
+    log(f"swap: {nblk} blocks of {16 * Hkv * d * 2} B per pool (K and V), device pool "
+        f"{Nd} blocks, pinned host pool {nblk} blocks")
+    kd = torch.randn((Nd, 16, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    vd = torch.randn((Nd, 16, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    kh = torch.empty((nblk, 16, Hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty((nblk, 16, Hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    src = rng.choice(Nd, size=nblk, replace=False)            # scattered device blocks
+    out_pairs = torch.from_numpy(np.stack([src, np.arange(nblk)], 1).astype(np.int64)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(nblk), src], 1).astype(np.int64)).cuda()
+    moved = 2 * kd[0].numel() * kd.element_size() * nblk      # K and V bytes per direction
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_out, t_in = [], []
+    for i in range(args.warmup + args.steps):
+        ev[0].record()
+        pa.pa_block_swap(kh, vh, kd, vd, out_pairs)
+        ev[1].record()
+        pa.pa_block_swap(kd, vd, kh, vh, in_pairs)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            t_out.append(ev[0].elapsed_time(ev[1]))
+            t_in.append(ev[1].elapsed_time(ev[2]))
+    ms_out, ms_in = sum(t_out) / len(t_out), sum(t_in) / len(t_in)
+    g_out, g_in = moved / ms_out / 1e6, moved / ms_in / 1e6
+    log(f"swap-out {ms_out:.3f} ms ({g_out:.1f} GB/s), swap-in {ms_in:.3f} ms ({g_in:.1f} GB/s)")
+    # a round trip must leave the device blocks as they were
+    ok = bool(torch.equal(kd[torch.from_numpy(src).cuda()].view(torch.int16),
+                          kh.cuda().view(torch.int16)))
+    record = {
+        "metric": "paged KV block swap GB/s per direction (device <-> pinned host), 8B GQA bf16 blocks",
+        "value": min(g_out, g_in), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_out + ms_in, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (torch.randn on device, seeded block choice)",
+        "config": {"workload": "swap_1gib_llama3_8b_blocks", "blocks": nblk, "kv_heads": Hkv,
+                   "head_dim": d, "block_size": 16, "bytes_per_direction": moved},
+        "swap_out_gbs": g_out, "swap_in_gbs": g_in, "round_trip_exact": ok,
+        "roofline": {"kernel": "pa_block_swap (block_swap_kernel)", "bound": "pcie",
+                     "achieved": min(g_out, g_in), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": min(g_out, g_in) / PCIE_PEAK_GBS, "traffic": None,
+                     "launch_ms": max(ms_out, ms_in), "algorithmic_bytes_per_launch": moved},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(record), flush=True)
+    return 0 if ok else 1
+
+
+def run_manager(args) -> int:
+    import numpy as np
+
+    import paged_kv_cache_367_amd as pa
+    import workload as wl
+
+    L = wl.config_lengths(3).astype(np.int64)
+    B = L.size
+    nblk = int(((L + 15) // 16).sum() * 1.1) + B * ((args.steps + args.warmup) // 16 + 2)
+    rng = np.random.default_rng(367)
+
+    def setup(m):
+        for b in range(B):
+            m.add(b, rng.integers(0, 32000, size=int(L[b])).tolist())
+
+    m = pa.BlockManager(nblk, 16, True)
+    setup(m)
+    width = int((L.max() + args.steps + args.warmup) // 16 + 2)
+    ids = np.arange(B, dtype=np.int64)
+    toks = rng.integers(0, 32000, size=(args.warmup + args.steps, B))
+    for i in range(args.warmup):
+        m.append_batch(ids, toks[i])
+        m.tables(ids, width)
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        m.append_batch(ids, toks[i])
+        m.tables(ids, width)
+    dt = (time.perf_counter() - t0) / args.steps
+    log(f"manager: {dt * 1e6:.1f} us per decode step of {B} appends + table export")
+    record = {
+        "metric": "paged KV block-manager decode-step bookkeeping, steps/s (256 sequences)",
+        "value": 1.0 / dt, "unit": "steps/s", "n_gpus": 0, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic (lengths of the Llama-3-8B workload, random token ids)",
+        "config": {"workload": "manager_decode_step_llama3_8b", "batch": B, "blocks": nblk,
+                   "block_size": 16, "prefix_cache": True,
+                   "calls_per_step": "pa_bm_append_batch + pa_bm_tables"},
+        "roofline": None, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.block_manager as obm
+        r = obm.BlockManager(nblk, 16, True)
+        rng = np.random.default_rng(367)
+        for b in range(B):
+            r.add(b, rng.integers(0, 32000, size=int(L[b])).tolist())
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_budget_s, 10.0) and n < args.steps:
+            for b in range(B):
+                r.append(b, int(toks[n, b]))
+            [r.table(b, width) for b in range(B)]
+            n += 1
+        rdt = (time.perf_counter() - t0) / max(n, 1)
+        record["cpu_baseline"] = {"value": 1.0 / rdt, "unit": "steps/s", "cores": 1,
+                                  "kind": "oracle", "sample": f"{n} decode steps of {B} appends"}
+    print(json.dumps(record), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,8 +390,9 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None,
                     help="tokens per split-KV partition (default: the workload's, else the library's)")
     ap.add_argument("--replicas", type=int, default=3)
-    ap.add_argument("--path", choices=["decode", "prefill"], default="decode",
-                    help="decode (the default step) or one chunked-prefill step")
+    ap.add_argument("--path", choices=["decode", "prefill", "swap", "manager"], default="decode",
+                    help="decode (the default step), one chunked-prefill step, a block swap "
+                         "to pinned host memory and back, or the host block manager")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -272,6 +406,9 @@ def main() -> int:
               f"(WORLD_SIZE={world}) is not supported. Each GPU would own a disjoint set of "
               "sequences and pool blocks, so no multi-GPU figure is produced.", file=sys.stderr)
         return 2
+
+    if args.path == "manager":                 # host bookkeeping only: no GPU needed
+        return run_manager(args)
 
     import numpy as np
     import torch
@@ -297,6 +434,8 @@ def main() -> int:
 
     if args.path == "prefill":
         return run_prefill(args)
+    if args.path == "swap":
+        return run_swap(args)
 
     log(f"building workload {args.config}")
     t0 = time.perf_counter()

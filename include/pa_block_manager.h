@@ -79,6 +79,16 @@ int32_t pa_bm_add(pa_block_manager_t* bm, int64_t seq_id, const int32_t* tokens,
 int32_t pa_bm_append(pa_block_manager_t* bm, int64_t seq_id, int32_t token, int64_t* slot,
                      int64_t* cow_src, int64_t* cow_dst);
 
+/* One decode step's appends in a single call: token tokens[i] to sequence seq_ids[i], in
+ * order, exactly as n calls of pa_bm_append. slots[i] receives each token's slot; the
+ * copy-on-write pairs are packed into cow_pairs[2 * k] (src, dst), k = *num_cow (at most n),
+ * ready for one pa_block_copy before the step's pa_cache_write. Stops at the first failing
+ * append: *done (required) receives the number applied, which stay applied, and the
+ * failure's code is returned (PA_OK when all n are done). */
+int32_t pa_bm_append_batch(pa_block_manager_t* bm, const int64_t* seq_ids,
+                           const int32_t* tokens, int32_t n, int64_t* slots, int64_t* cow_pairs,
+                           int32_t* num_cow, int32_t* done);
+
 /* New sequence child sharing every block of parent (each count + 1): parallel sampling
  * and beam-search forks. */
 int32_t pa_bm_fork(pa_block_manager_t* bm, int64_t parent_id, int64_t child_id);

@@ -32,6 +32,8 @@ def _lib():
         lib.pa_bm_add.argtypes = [P, I64, pi32, I32, U64, pi32]
         lib.pa_bm_append.restype = I32
         lib.pa_bm_append.argtypes = [P, I64, I32, pi64, pi64, pi64]
+        lib.pa_bm_append_batch.restype = I32
+        lib.pa_bm_append_batch.argtypes = [P, pi64, pi32, I32, pi64, pi64, pi32, pi32]
         lib.pa_bm_fork.restype = I32
         lib.pa_bm_fork.argtypes = [P, I64, I64]
         lib.pa_bm_free.restype = I32
@@ -109,6 +111,25 @@ class BlockManager:
         _check(self._lib.pa_bm_append(self._h, int(seq_id), int(token), ctypes.byref(slot),
                                       ctypes.byref(src), ctypes.byref(dst)), "pa_bm_append")
         return slot.value, src.value, dst.value
+
+    def append_batch(self, seq_ids, tokens):
+        """One step's appends in one call: returns (slots int64 [n], cow pairs int64 [k, 2]).
+        On a failure raises PaError with .done = the number of appends applied."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        if ids.shape != tok.shape:
+            raise ValueError("one token per sequence id")
+        slots = np.empty(ids.size, dtype=np.int64)
+        pairs = np.empty((max(ids.size, 1), 2), dtype=np.int64)
+        k, done = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = self._lib.pa_bm_append_batch(self._h, _i64p(ids), _i32p(tok), ids.size,
+                                          _i64p(slots), _i64p(pairs), ctypes.byref(k),
+                                          ctypes.byref(done))
+        if st < 0:
+            err = PaError(st, "pa_bm_append_batch")
+            err.done = done.value
+            raise err
+        return slots, pairs[:k.value].copy()
 
     def fork(self, parent: int, child: int):
         _check(self._lib.pa_bm_fork(self._h, int(parent), int(child)), "pa_bm_fork")

@@ -10,6 +10,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <deque>
 #include <new>
 #include <unordered_map>
@@ -219,6 +220,30 @@ int32_t pa_bm_append(pa_block_manager_t* bm, int64_t seq_id, int32_t token, int6
   return PA_OK;
 }
 
+int32_t pa_bm_append_batch(pa_block_manager_t* bm, const int64_t* seq_ids,
+                           const int32_t* tokens, int32_t n, int64_t* slots, int64_t* cow_pairs,
+                           int32_t* num_cow, int32_t* done) {
+  if (!bm || !done) return PA_ERR_NULL;
+  *done = 0;
+  if (num_cow) *num_cow = 0;
+  if (n < 0) return PA_ERR_SHAPE;
+  if (n > 0 && (!seq_ids || !tokens || !slots || !cow_pairs || !num_cow)) return PA_ERR_NULL;
+  int32_t k = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t src, dst;
+    const int32_t st = pa_bm_append(bm, seq_ids[i], tokens[i], &slots[i], &src, &dst);
+    if (st != PA_OK) return st;
+    if (src >= 0) {
+      cow_pairs[2 * k] = src;
+      cow_pairs[2 * k + 1] = dst;
+      ++k;
+      *num_cow = k;
+    }
+    *done = i + 1;
+  }
+  return PA_OK;
+}
+
 int32_t pa_bm_fork(pa_block_manager_t* bm, int64_t parent_id, int64_t child_id) {
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(parent_id);
@@ -279,17 +304,20 @@ int32_t pa_bm_tables(const pa_block_manager_t* bm, const int64_t* seq_ids, int32
   if (!bm) return PA_ERR_NULL;
   if (n < 0 || width < 0) return PA_ERR_SHAPE;
   if (n > 0 && (!seq_ids || !tables || !context_lens)) return PA_ERR_NULL;
+  std::vector<const Seq*> seqs(n);
   for (int32_t i = 0; i < n; ++i) {          // check everything before writing anything
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
     if (it->second.swapped) return PA_ERR_UNSUPPORTED;
     if ((int32_t)it->second.blocks.size() > width) return PA_ERR_SHAPE;
+    seqs[i] = &it->second;
   }
   for (int32_t i = 0; i < n; ++i) {
-    const Seq& s = bm->seqs.find(seq_ids[i])->second;
-    for (int32_t j = 0; j < width; ++j)
-      tables[(size_t)i * width + j] = j < (int32_t)s.blocks.size() ? s.blocks[j] : -1;
-    context_lens[i] = (int32_t)s.tokens.size();
+    const std::vector<int32_t>& b = seqs[i]->blocks;
+    int32_t* row = tables + (size_t)i * width;
+    if (!b.empty()) memcpy(row, b.data(), sizeof(int32_t) * b.size());
+    std::fill(row + b.size(), row + width, -1);
+    context_lens[i] = (int32_t)seqs[i]->tokens.size();
   }
   return PA_OK;
 }
