@@ -27,7 +27,7 @@ Every function is pinned by tests in tests/test_oracle_*.py against values the p
 print, closed forms, library routines and brute force.
 """
 from .storage import decode_storage, e4m3_table, bf16_bits_to_f64
-from .attention import decode_ref, attend, gather_sequence, kv_head_of
+from .attention import decode_ref, attend, gather_sequence, head_scales, kv_head_of
 from .cache_ops import cache_write_ref, block_copy_ref, block_swap_ref
 from .quantize import e4m3_encode, quant_inputs, cache_write_fp8_ref
 from .prefill import prefill_ref, query_positions
@@ -35,7 +35,7 @@ from .formulas import kv_bytes_per_token, kv_bytes_per_request
 
 __all__ = [
     "decode_storage", "e4m3_table", "bf16_bits_to_f64",
-    "decode_ref", "attend", "gather_sequence", "kv_head_of",
+    "decode_ref", "attend", "gather_sequence", "head_scales", "kv_head_of",
     "cache_write_ref", "block_copy_ref", "block_swap_ref",
     "e4m3_encode", "quant_inputs", "cache_write_fp8_ref",
     "prefill_ref", "query_positions",

@@ -65,13 +65,25 @@ def attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
     return p @ V, p
 
 
+def head_scales(s, num_kv_heads: int) -> np.ndarray:
+    """A dequantisation scale per kv head, shaped [Hkv, 1] to multiply [..., Hkv, d]: one
+    number for the whole tensor, or one per kv head (each head's codes times its own)."""
+    a = np.asarray(s, dtype=np.float64).reshape(-1)
+    if a.size == 1:
+        a = np.full(num_kv_heads, a[0])
+    if a.size != num_kv_heads:
+        raise ValueError("one scale, or one per kv head")
+    return a.reshape(num_kv_heads, 1)
+
+
 def decode_ref(q, k_pool, v_pool, block_tables, context_lens, scale, *, q_kind, kv_kind,
-               k_scale: float = 1.0, v_scale: float = 1.0, seqs: Optional[Iterable[int]] = None,
+               k_scale=1.0, v_scale=1.0, seqs: Optional[Iterable[int]] = None,
                return_probs: bool = False):
     """Reference decode output, float64 [len(seqs) or B, Hq, d].
 
     q: storage [B, Hq, d]; k_pool/v_pool: storage [N, bs, Hkv, d];
     block_tables: int [B, maxb] (-1 padding); context_lens: int [B].
+    k_scale, v_scale: dequantisation scales, one number or one per kv head.
     seqs restricts the computation to a subset of sequences (in that order)."""
     B, Hq, d = q.shape
     N, bs, Hkv, dk = k_pool.shape
@@ -80,6 +92,7 @@ def decode_ref(q, k_pool, v_pool, block_tables, context_lens, scale, *, q_kind, 
     if Hq % Hkv:
         raise ValueError("query heads must be a multiple of kv heads")
     G = Hq // Hkv
+    ks, vs = head_scales(k_scale, Hkv), head_scales(v_scale, Hkv)
     order = list(range(B)) if seqs is None else [int(b) for b in seqs]
     out = np.zeros((len(order), Hq, d), dtype=np.float64)
     probs = {}
@@ -87,8 +100,8 @@ def decode_ref(q, k_pool, v_pool, block_tables, context_lens, scale, *, q_kind, 
         L = int(context_lens[b])
         if L <= 0:
             continue
-        K = decode_storage(gather_sequence(k_pool, block_tables[b], L, bs, N), kv_kind) * k_scale
-        V = decode_storage(gather_sequence(v_pool, block_tables[b], L, bs, N), kv_kind) * v_scale
+        K = decode_storage(gather_sequence(k_pool, block_tables[b], L, bs, N), kv_kind) * ks
+        V = decode_storage(gather_sequence(v_pool, block_tables[b], L, bs, N), kv_kind) * vs
         qb = decode_storage(q[b], q_kind)
         for h in range(Hq):
             g = kv_head_of(h, G)

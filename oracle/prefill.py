@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attend, gather_sequence, kv_head_of
+from .attention import attend, gather_sequence, head_scales, kv_head_of
 from .storage import decode_storage
 
 
@@ -30,13 +30,14 @@ def query_positions(L: int, n: int) -> np.ndarray:
 
 
 def prefill_ref(q, query_start, k_pool, v_pool, block_tables, context_lens, scale, *,
-                q_kind, kv_kind, k_scale: float = 1.0, v_scale: float = 1.0, rows=None):
+                q_kind, kv_kind, k_scale=1.0, v_scale=1.0, rows=None):
     """Reference output, float64 [total query tokens, Hq, d].
 
     q: storage [Tq, Hq, d]; query_start: int [B + 1], non-decreasing, query_start[B] = Tq;
     k_pool/v_pool: storage [N, bs, Hkv, d]; block_tables: int [B, maxb];
-    context_lens: int [B]; rows: optional collection of query rows to compute (the others
-    are left NaN), for sampled checks of large inputs."""
+    context_lens: int [B]; k_scale, v_scale: one number or one per kv head; rows: optional
+    collection of query rows to compute (the others are left NaN), for sampled checks of
+    large inputs."""
     Tq, Hq, d = q.shape
     N, bs, Hkv, dk = k_pool.shape
     if dk != d or v_pool.shape != k_pool.shape or Hq % Hkv:
@@ -45,6 +46,7 @@ def prefill_ref(q, query_start, k_pool, v_pool, block_tables, context_lens, scal
     if qs[0] != 0 or qs[-1] != Tq or np.any(np.diff(qs) < 0):
         raise ValueError("query_start must rise from 0 to the number of query rows")
     G = Hq // Hkv
+    ks, vs = head_scales(k_scale, Hkv), head_scales(v_scale, Hkv)
     want = None if rows is None else set(int(r) for r in rows)
     out = np.zeros((Tq, Hq, d), dtype=np.float64)
     if want is not None:
@@ -54,8 +56,8 @@ def prefill_ref(q, query_start, k_pool, v_pool, block_tables, context_lens, scal
         pos = query_positions(L, n)
         if n == 0 or (want is not None and not want & set(range(qs[b], qs[b + 1]))):
             continue
-        K = decode_storage(gather_sequence(k_pool, block_tables[b], L, bs, N), kv_kind) * k_scale
-        V = decode_storage(gather_sequence(v_pool, block_tables[b], L, bs, N), kv_kind) * v_scale
+        K = decode_storage(gather_sequence(k_pool, block_tables[b], L, bs, N), kv_kind) * ks
+        V = decode_storage(gather_sequence(v_pool, block_tables[b], L, bs, N), kv_kind) * vs
         qb = decode_storage(q[qs[b]:qs[b + 1]], q_kind)
         for i in range(n):
             if want is not None and int(qs[b]) + i not in want:

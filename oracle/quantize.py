@@ -32,10 +32,17 @@ from .storage import decode_storage, e4m3_table
 E4M3_MAX = 448.0
 
 
-def quant_inputs(new: np.ndarray, kind: str, scale: float) -> np.ndarray:
-    """The binary32 values y = fp32(fp32(x) * fp32(1 / scale)) that get encoded."""
+def quant_inputs(new: np.ndarray, kind: str, scale) -> np.ndarray:
+    """The binary32 values y = fp32(fp32(x) * fp32(1 / scale)) that get encoded; new is
+    [T, Hkv, d] and scale one number or one per kv head (head g divided by its own)."""
     x = decode_storage(new, kind).astype(np.float32)        # exact: every source is binary32-representable
-    inv = np.float32(1.0) / np.float32(scale)
+    s = np.asarray(scale, dtype=np.float32).reshape(-1)
+    if s.size == 1:
+        inv = np.float32(1.0) / s[0]                        # one binary32 division
+    elif x.ndim >= 2 and s.size == x.shape[-2]:
+        inv = (np.float32(1.0) / s).reshape(-1, 1)          # one per kv head
+    else:
+        raise ValueError("one scale, or one per kv head")
     with np.errstate(over="ignore", invalid="ignore"):
         return x * inv
 
@@ -71,10 +78,11 @@ def e4m3_encode(y: np.ndarray) -> np.ndarray:
     return out.reshape(y.shape)
 
 
-def cache_write_fp8_ref(pool: np.ndarray, new: np.ndarray, kind: str, scale: float,
+def cache_write_fp8_ref(pool: np.ndarray, new: np.ndarray, kind: str, scale,
                         slot_mapping: np.ndarray) -> np.ndarray:
     """fp8 pool [N, bs, Hkv, d] (uint8), new rows [T, Hkv, d] in storage encoding `kind`
-    (f32, f16 or bf16 bits), per-tensor dequantisation scale, slots [T] (-1 = skip) ->
+    (f32, f16 or bf16 bits), dequantisation scale (per tensor, or per kv head), slots [T]
+    (-1 = skip) ->
     updated copy of the pool with row s written as the E4M3 codes of the new row."""
     N, bs = pool.shape[:2]
     out = np.array(pool, dtype=np.uint8, copy=True)

@@ -793,4 +793,50 @@ def pin_bm_swap_preemption_keeps_contents():
     assert slot // 4 == m.table(0, 5)[4]
 
 
+# ----------------------------------------------------------------------------- per-head scales
+
+def _fp8_case(seed=31, Hkv=4, G=2, d=64):
+    w = wl.custom(batch=3, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=d,
+                  kv_dtype="fp8_e4m3", context_lens=[5, 40, 77], seed=seed)
+    return w
+
+
+def pin_head_scales_equal_reduce_to_tensor():
+    """One scale per kv head, all equal, is the per-tensor scale, bit for bit (decode and
+    multi-token queries)."""
+    w = _fp8_case()
+    args = (w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale)
+    kw = dict(q_kind="bf16", kv_kind="fp8_e4m3")
+    a = oracle.decode_ref(*args, k_scale=0.03, v_scale=0.5, **kw)
+    b = oracle.decode_ref(*args, k_scale=[0.03] * 4, v_scale=[0.5] * 4, **kw)
+    assert np.array_equal(a, b)
+    qs = np.array([0, 1, 2, 3])
+    a = oracle.prefill_ref(w.q, qs, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                           k_scale=0.03, v_scale=0.5, **kw)
+    b = oracle.prefill_ref(w.q, qs, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                           k_scale=[0.03] * 4, v_scale=[0.5] * 4, **kw)
+    assert np.array_equal(a, b)
+
+
+def pin_head_scales_reach_their_own_heads():
+    """kv head g uses scale[g]: with distinct per-head scales, the query heads of kv head g
+    equal (bit for bit) a per-tensor run at scale[g]; the same for quantisation, head by
+    head."""
+    import oracle.quantize as qz
+    w = _fp8_case(seed=32)
+    ks, vs = [0.01, 0.02, 0.05, 0.11], [0.3, 0.7, 1.9, 0.05]
+    kw = dict(q_kind="bf16", kv_kind="fp8_e4m3")
+    args = (w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale)
+    per_head = oracle.decode_ref(*args, k_scale=ks, v_scale=vs, **kw)
+    G = 2
+    for g in range(4):
+        one = oracle.decode_ref(*args, k_scale=ks[g], v_scale=vs[g], **kw)
+        assert np.array_equal(per_head[:, g * G:(g + 1) * G], one[:, g * G:(g + 1) * G])
+    rng = np.random.default_rng(33)
+    new = rng.standard_normal((5, 4, 64)).astype(np.float32) * 3
+    codes = qz.e4m3_encode(qz.quant_inputs(new, "f32", ks))
+    for g in range(4):
+        assert np.array_equal(codes[:, g], qz.e4m3_encode(qz.quant_inputs(new[:, g], "f32", ks[g])))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

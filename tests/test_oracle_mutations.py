@@ -216,6 +216,13 @@ def _swap_out_pairs_reversed(self, seq_id):
     return [(h, d) for d, h in _good_swap_out(self, seq_id)]
 
 
+_good_head_scales = att.head_scales
+
+
+def _head_scales_reversed(s, num_kv_heads):
+    return _good_head_scales(s, num_kv_heads)[::-1].copy()    # head g gets scale[Hkv-1-g]
+
+
 MUTATIONS = {
     "gqa_interleaved": (att, "kv_head_of", _interleaved_gqa),
     "no_length_mask": (att, "gather_sequence", _no_truncation),
@@ -240,6 +247,7 @@ MUTATIONS = {
     "bm_block_per_token": (obm.BlockManager, "append", _append_new_block_each_token),
     "bm_evicts_most_recent": (obm.BlockManager, "_allocate", _allocate_evicts_most_recent),
     "swap_pair_reversed": (cops, "block_swap_ref", _swap_reversed),
+    "head_scales_reversed": (att, "head_scales", _head_scales_reversed),
     "bm_swap_out_pairs_reversed": (obm.BlockManager, "swap_out", _swap_out_pairs_reversed),
 }
 
