@@ -199,6 +199,27 @@ pa_status_t pa_prefill(const pa_prefill_desc_t* desc, void* out, const void* q,
                        int32_t max_query_len, float scale, float k_scale, float v_scale,
                        void* stream);
 
+/* Per-head dequantisation scales (the fp8 KV cache row's "per-head scales"): the same as
+ * pa_decode and pa_prefill, except that kv head g's K codes are multiplied by k_scales[g]
+ * and its V codes by v_scales[g] instead of one k_scale / v_scale for the whole pool.
+ * k_scales, v_scales: DEVICE arrays of Hkv floats (finite and > 0: the caller's contract;
+ * the library cannot check device values), 4-byte aligned; required (non-NULL) whenever the
+ * call has work. pa_decode_head_scales takes fp8 E4M3 pools only (other kv dtypes:
+ * UNSUPPORTED); pa_prefill_head_scales any supported kv dtype. With all scales equal the
+ * results are bitwise those of the per-tensor calls. */
+pa_status_t pa_decode_head_scales(const pa_decode_desc_t* desc, void* out, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t max_context_len, float scale, const float* k_scales,
+                                  const float* v_scales, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+pa_status_t pa_prefill_head_scales(const pa_prefill_desc_t* desc, void* out, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start, int32_t max_query_len,
+                                   float scale, const float* k_scales, const float* v_scales,
+                                   void* stream);
+
 /* Slot write of new tokens (reshape_and_cache): a generated token occupies one slot
  * (vLLM-PagedAttention与连续批处理技术拆解, section 3.1). For each t < num_tokens with
  * slot_mapping[t] = s >= 0:
@@ -232,6 +253,19 @@ pa_status_t pa_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new, co
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t src_dtype, float k_scale,
                                float v_scale, void* stream);
+
+/* The same with one scale per kv head: element x of kv head g quantises with
+ * y = fp32(x) * fp32(1 / k_scales[g]) (the reciprocal rounded to nearest, as the host
+ * rounds it for pa_cache_write_fp8), V likewise with v_scales[g]. k_scales, v_scales:
+ * DEVICE arrays of Hkv floats, finite and > 0 (caller's contract), 4-byte aligned, required
+ * when num_tokens > 0; head_dim must be a multiple of 8 (else UNSUPPORTED). */
+pa_status_t pa_cache_write_fp8_head_scales(void* k_pool, void* v_pool, const void* k_new,
+                                           const void* v_new, const int64_t* slot_mapping,
+                                           int32_t num_tokens, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t src_dtype,
+                                           const float* k_scales, const float* v_scales,
+                                           void* stream);
 
 /* Copy-on-write block copy: a shared block is read-only and a sequence that must write
  * into it copies it first (vLLM-PagedAttention与连续批处理技术拆解, section 3.4). For

@@ -60,6 +60,14 @@ def load_library():
     lib.pa_decode_workspace_bytes.argtypes = [D, I32]
     lib.pa_decode.restype = I32
     lib.pa_decode.argtypes = [D, P, P, P, P, P, P, I32, F, F, F, P, SZ, P]
+    lib.pa_decode_head_scales.restype = I32
+    lib.pa_decode_head_scales.argtypes = [D, P, P, P, P, P, P, I32, F, P, P, P, SZ, P]
+    lib.pa_prefill_head_scales.restype = I32
+    lib.pa_prefill_head_scales.argtypes = [ctypes.POINTER(PrefillDesc), P, P, P, P, P, P, P,
+                                           I32, F, P, P, P]
+    lib.pa_cache_write_fp8_head_scales.restype = I32
+    lib.pa_cache_write_fp8_head_scales.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                                   P, P, P]
     lib.pa_prefill.restype = I32
     lib.pa_prefill.argtypes = [ctypes.POINTER(PrefillDesc), P, P, P, P, P, P, P, I32, F, F, F, P]
     lib.pa_cache_write.restype = I32
@@ -141,12 +149,27 @@ def pa_decode_workspace_bytes(desc: DecodeDesc, max_context_len: int) -> int:
     return load_library().pa_decode_workspace_bytes(ctypes.byref(desc), max_context_len)
 
 
+def _head_scale_ptrs(k_scale, v_scale, num_kv_heads):
+    """(per-tensor floats, per-head pointers): GPU float32 tensors of Hkv values select the
+    per-head entry points."""
+    import torch
+    per_head = isinstance(k_scale, torch.Tensor) or isinstance(v_scale, torch.Tensor)
+    if not per_head:
+        return False, float(k_scale), float(v_scale), None, None
+    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or \
+                t.shape != (num_kv_heads,):
+            raise ValueError(f"{name}: per-head scales are float32 [num_kv_heads] GPU tensors")
+    return True, 1.0, 1.0, _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale")
+
+
 def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
-              scale: float, k_scale: float = 1.0, v_scale: float = 1.0, workspace=None,
+              scale: float, k_scale=1.0, v_scale=1.0, workspace=None,
               partition_size: int = 0, stream=None):
     """Decode attention into `out` [B, Hq, d]. workspace: a zero-initialised uint8 GPU
     tensor of at least pa_decode_workspace_bytes() bytes (allocated here, zero-filled,
-    when None)."""
+    when None). k_scale / v_scale: floats, or float32 [Hkv] GPU tensors of per-head scales
+    (pa_decode_head_scales)."""
     import torch
     lib = load_library()
     if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
@@ -161,22 +184,26 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_le
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.pa_decode(ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
-                       _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
-                       _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
-                       float(scale), float(k_scale), float(v_scale), ws_ptr, ws_bytes,
-                       _stream(stream))
+    per_head, ks, vs, kp, vp = _head_scale_ptrs(k_scale, v_scale, k_pool.shape[2])
+    common = (ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+              _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
+              _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
+              float(scale))
+    if per_head:
+        st = lib.pa_decode_head_scales(*common, kp, vp, ws_ptr, ws_bytes, _stream(stream))
+    else:
+        st = lib.pa_decode(*common, ks, vs, ws_ptr, ws_bytes, _stream(stream))
     if st != 0:
-        raise PaError(st, "pa_decode")
+        raise PaError(st, "pa_decode_head_scales" if per_head else "pa_decode")
     return out
 
 
 def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
-               max_query_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-               stream=None):
+               max_query_len: int, scale: float, k_scale=1.0, v_scale=1.0, stream=None):
     """Multi-token causal attention into `out` [Tq, Hq, d] for packed query rows q
     [Tq, Hq, d]; sequence b owns rows query_start[b] .. query_start[b+1] - 1 (int32
-    [B + 1]), the last tokens of its context_lens[b] cached ones."""
+    [B + 1]), the last tokens of its context_lens[b] cached ones. k_scale / v_scale: floats,
+    or float32 [Hkv] GPU tensors of per-head scales (pa_prefill_head_scales)."""
     import torch
     lib = load_library()
     if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
@@ -192,14 +219,17 @@ def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
         raise ValueError("head_dim of q and the pool differ")
     desc = PrefillDesc(B, Tq, Hq, Hkv, d, bs, N, block_tables.shape[1], dtype_code(q),
                        dtype_code(k_pool), dtype_code(out))
-    st = lib.pa_prefill(ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"),
-                        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-                        _dev(block_tables, "block_tables", torch.int32),
-                        _dev(context_lens, "context_lens", torch.int32),
-                        _dev(query_start, "query_start", torch.int32), int(max_query_len),
-                        float(scale), float(k_scale), float(v_scale), _stream(stream))
+    per_head, ks, vs, kp, vp = _head_scale_ptrs(k_scale, v_scale, Hkv)
+    common = (ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"),
+              _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
+              _dev(context_lens, "context_lens", torch.int32),
+              _dev(query_start, "query_start", torch.int32), int(max_query_len), float(scale))
+    if per_head:
+        st = lib.pa_prefill_head_scales(*common, kp, vp, _stream(stream))
+    else:
+        st = lib.pa_prefill(*common, ks, vs, _stream(stream))
     if st != 0:
-        raise PaError(st, "pa_prefill")
+        raise PaError(st, "pa_prefill_head_scales" if per_head else "pa_prefill")
     return out
 
 
@@ -223,8 +253,8 @@ def pa_cache_write(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
 def pa_cache_write_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale=1.0, v_scale=1.0,
                        stream=None):
     """Write new tokens' K/V [T, Hkv, d] (float32, float16 or bfloat16) into the slots of
-    fp8 E4M3 pools (uint8 or float8_e4m3fn), quantising with per-tensor dequantisation
-    scales k_scale, v_scale."""
+    fp8 E4M3 pools (uint8 or float8_e4m3fn), quantising with dequantisation scales k_scale,
+    v_scale: floats (per tensor) or float32 [Hkv] GPU tensors (per kv head)."""
     import torch
     lib = load_library()
     N, bs, Hkv, d = k_pool.shape
@@ -236,13 +266,16 @@ def pa_cache_write_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale=1.0, 
         raise ValueError("pools must be fp8 E4M3 bytes of the same shape")
     if v_new.dtype != k_new.dtype:
         raise ValueError("k_new and v_new must share a dtype")
-    st = lib.pa_cache_write_fp8(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-                                _dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                                _dev(slot_mapping, "slot_mapping", torch.int64), T, Hkv, d, bs,
-                                N, dtype_code(k_new), float(k_scale), float(v_scale),
-                                _stream(stream))
+    per_head, ks, vs, kp, vp = _head_scale_ptrs(k_scale, v_scale, Hkv)
+    common = (_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+              _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping", torch.int64), T, Hkv, d,
+              bs, N, dtype_code(k_new))
+    if per_head:
+        st = lib.pa_cache_write_fp8_head_scales(*common, kp, vp, _stream(stream))
+    else:
+        st = lib.pa_cache_write_fp8(*common, ks, vs, _stream(stream))
     if st != 0:
-        raise PaError(st, "pa_cache_write_fp8")
+        raise PaError(st, "pa_cache_write_fp8_head_scales" if per_head else "pa_cache_write_fp8")
 
 
 def pa_block_copy(k_pool, v_pool, src_dst_pairs, stream=None):

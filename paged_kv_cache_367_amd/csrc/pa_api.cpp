@@ -143,11 +143,18 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_conte
   return w.total;
 }
 
-pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
-                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                      const int32_t* context_lens, int32_t max_context_len, float scale,
-                      float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_decode_head_scales: per-tensor scales, or (k_heads, v_heads) device
+// arrays of one scale per kv head (then k_scale = v_scale = 1 here)
+pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
+                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t max_context_len, float scale,
+                        float k_scale, float v_scale, const float* k_heads,
+                        const float* v_heads, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   pa_status_t st = check_desc(desc, max_context_len);
   if (st != PA_OK) return st;
   if (desc->batch == 0) return PA_OK;
@@ -182,8 +189,11 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
   a.max_context_len = max_context_len;
   a.num_ranges = W;
   a.part_units = part_units(desc);
-  a.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.qk_scale_log2 = scale * k_scale * pa::kLog2e;
   a.v_scale = v_scale;
+  a.k_head_scales = k_heads;
+  a.v_head_scales = v_heads;
+  a.qk_scale = scale;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = desc->num_q_heads / desc->num_kv_heads;
@@ -202,16 +212,50 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
   m.num_ranges = W;
   m.part_units = a.part_units;
   m.v_scale = v_scale;
+  m.v_head_scales = v_heads;
   if (pa::launch_merge(desc->out_dtype, desc->head_dim, group, m, s) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;
 }
 
-pa_status_t pa_prefill(const pa_prefill_desc_t* desc, void* out, const void* q,
-                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                       const int32_t* context_lens, const int32_t* query_start,
-                       int32_t max_query_len, float scale, float k_scale, float v_scale,
-                       void* stream) {
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
+                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t max_context_len, float scale,
+                      float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                     scale, k_scale, v_scale, nullptr, nullptr, workspace, workspace_bytes,
+                     stream);
+}
+
+pa_status_t pa_decode_head_scales(const pa_decode_desc_t* desc, void* out, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t max_context_len, float scale, const float* k_scales,
+                                  const float* v_scales, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (desc && desc->batch > 0 && (!k_scales || !v_scales)) return PA_ERR_NULL;
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4)) return PA_ERR_ALIGN;
+  // per-head scales are built for fp8 pools (the per-head kernels are fp8 instantiations)
+  if (desc && desc->kv_dtype != PA_FP8_E4M3 && valid_dtype(desc->kv_dtype))
+    return PA_ERR_UNSUPPORTED;
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                     scale, 1.0f, 1.0f, k_scales, v_scales, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status_t prefill_impl(const pa_prefill_desc_t* desc, void* out, const void* q,
+                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         const int32_t* context_lens, const int32_t* query_start,
+                         int32_t max_query_len, float scale, float k_scale, float v_scale,
+                         const float* k_heads, const float* v_heads, void* stream) {
   const pa_prefill_desc_t* d = desc;
   if (!d) return PA_ERR_NULL;
   if (d->batch < 0 || d->num_query_tokens < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
@@ -263,12 +307,41 @@ pa_status_t pa_prefill(const pa_prefill_desc_t* desc, void* out, const void* q,
   a.max_query_len = max_query_len;
   a.num_q_tiles = (int32_t)tiles;
   a.num_workgroups = (int32_t)(groups * tiles * 8);
-  a.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.qk_scale_log2 = scale * k_scale * pa::kLog2e;
   a.v_scale = v_scale;
+  a.k_head_scales = k_heads;
+  a.v_head_scales = v_heads;
+  a.qk_scale = scale;
   if (pa::launch_prefill(d->q_dtype, d->kv_dtype, d->out_dtype, d->head_dim, group, a,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_prefill(const pa_prefill_desc_t* desc, void* out, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start,
+                       int32_t max_query_len, float scale, float k_scale, float v_scale,
+                       void* stream) {
+  return prefill_impl(desc, out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                      max_query_len, scale, k_scale, v_scale, nullptr, nullptr, stream);
+}
+
+pa_status_t pa_prefill_head_scales(const pa_prefill_desc_t* desc, void* out, const void* q,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start, int32_t max_query_len,
+                                   float scale, const float* k_scales, const float* v_scales,
+                                   void* stream) {
+  if (desc && desc->batch > 0 && max_query_len > 0 && (!k_scales || !v_scales))
+    return PA_ERR_NULL;
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4)) return PA_ERR_ALIGN;
+  return prefill_impl(desc, out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                      max_query_len, scale, 1.0f, 1.0f, k_scales, v_scales, stream);
 }
 
 static pa_status_t check_cache_args(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -304,11 +377,16 @@ pa_status_t pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const 
   return PA_OK;
 }
 
-pa_status_t pa_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
-                               const int64_t* slot_mapping, int32_t num_tokens,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t num_blocks, int32_t src_dtype, float k_scale,
-                               float v_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t cache_write_fp8_impl(void* k_pool, void* v_pool, const void* k_new,
+                                 const void* v_new, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t src_dtype,
+                                 float k_scale, float v_scale, const float* k_heads,
+                                 const float* v_heads, void* stream) {
   int64_t row_bytes = 0;
   if (num_tokens < 0) return PA_ERR_SHAPE;
   pa_status_t st = check_cache_args(num_kv_heads, head_dim, block_size, num_blocks,
@@ -328,9 +406,39 @@ pa_status_t pa_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new, co
   const int64_t num_slots = (int64_t)num_blocks * block_size;
   if (pa::launch_cache_write_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
                                  (int32_t)row_bytes, num_slots, src_dtype, k_inv, v_inv,
+                                 k_heads, v_heads, head_dim,
                                  static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t src_dtype, float k_scale,
+                               float v_scale, void* stream) {
+  return cache_write_fp8_impl(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                              num_kv_heads, head_dim, block_size, num_blocks, src_dtype, k_scale,
+                              v_scale, nullptr, nullptr, stream);
+}
+
+pa_status_t pa_cache_write_fp8_head_scales(void* k_pool, void* v_pool, const void* k_new,
+                                           const void* v_new, const int64_t* slot_mapping,
+                                           int32_t num_tokens, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t src_dtype,
+                                           const float* k_scales, const float* v_scales,
+                                           void* stream) {
+  if (num_tokens > 0 && (!k_scales || !v_scales)) return PA_ERR_NULL;
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4)) return PA_ERR_ALIGN;
+  if (head_dim % 8 != 0) return PA_ERR_UNSUPPORTED;     // an 8-value piece stays in one head
+  return cache_write_fp8_impl(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                              num_kv_heads, head_dim, block_size, num_blocks, src_dtype, 1.0f,
+                              1.0f, k_scales, v_scales, stream);
 }
 
 pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,

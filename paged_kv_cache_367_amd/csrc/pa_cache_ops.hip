@@ -95,13 +95,21 @@ template <int SRC>
 __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const uint8_t* __restrict__ k_new,
     const uint8_t* __restrict__ v_new, const int64_t* __restrict__ slots, int32_t num_tokens,
-    int32_t row_octs, int64_t num_slots, float k_inv, float v_inv) {
+    int32_t row_octs, int64_t num_slots, float k_inv, float v_inv,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int32_t head_octs) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t t = idx / row_octs;
   if (t >= num_tokens) return;
   const int64_t c = idx - t * row_octs;              // 8-element piece of the row
   const int64_t s = slots[t];
   if (s < 0 || s >= num_slots) return;
+  if (k_scales) {
+    // per-head scales: the piece lies in kv head c / head_octs; one binary32 reciprocal,
+    // rounded to nearest like the host's for a per-tensor scale
+    const int64_t g = c / head_octs;
+    k_inv = __fdiv_rn(1.0f, k_scales[g]);
+    v_inv = __fdiv_rn(1.0f, v_scales[g]);
+  }
   const int64_t e = (t * row_octs + c) * 8;          // source element
   const int64_t dst = (s * row_octs + c) * 8;        // pool byte (one byte per element)
   *reinterpret_cast<u32x2*>(k_pool + dst) = quant8<SRC>(k_new, e, k_inv);
@@ -141,8 +149,10 @@ hipError_t launch_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new,
                                   const void* v_new, const int64_t* slot_mapping,
                                   int32_t num_tokens, int32_t row_elems, int64_t num_slots,
                                   int32_t src_dtype, float k_inv, float v_inv,
-                                  hipStream_t stream) {
+                                  const float* k_head_scales, const float* v_head_scales,
+                                  int32_t head_dim, hipStream_t stream) {
   const int32_t row_octs = row_elems / 8;
+  const int32_t head_octs = head_dim / 8;
   const int64_t total = (int64_t)num_tokens * row_octs;
   const dim3 grid((uint32_t)((total + 255) / 256)), block(256);
   auto* kp = static_cast<uint8_t*>(k_pool);
@@ -152,15 +162,18 @@ hipError_t launch_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new,
   switch (src_dtype) {
     case PA_F32:
       cache_write_fp8_kernel<PA_F32><<<grid, block, 0, stream>>>(
-          kp, vp, kn, vn, slot_mapping, num_tokens, row_octs, num_slots, k_inv, v_inv);
+          kp, vp, kn, vn, slot_mapping, num_tokens, row_octs, num_slots, k_inv, v_inv,
+          k_head_scales, v_head_scales, head_octs);
       break;
     case PA_F16:
       cache_write_fp8_kernel<PA_F16><<<grid, block, 0, stream>>>(
-          kp, vp, kn, vn, slot_mapping, num_tokens, row_octs, num_slots, k_inv, v_inv);
+          kp, vp, kn, vn, slot_mapping, num_tokens, row_octs, num_slots, k_inv, v_inv,
+          k_head_scales, v_head_scales, head_octs);
       break;
     case PA_BF16:
       cache_write_fp8_kernel<PA_BF16><<<grid, block, 0, stream>>>(
-          kp, vp, kn, vn, slot_mapping, num_tokens, row_octs, num_slots, k_inv, v_inv);
+          kp, vp, kn, vn, slot_mapping, num_tokens, row_octs, num_slots, k_inv, v_inv,
+          k_head_scales, v_head_scales, head_octs);
       break;
     default:
       return hipErrorInvalidValue;

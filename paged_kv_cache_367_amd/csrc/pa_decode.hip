@@ -236,7 +236,9 @@ struct UnitMeta {
   __device__ int chunk() const { return hc >> 12; }
 };
 
-template <int KV, int QT, int OT, int D, int G>
+// PH: per-head dequantisation scales (k_head_scales / v_head_scales); a separate
+// instantiation, so the per-tensor kernels carry no extra registers.
+template <int KV, int QT, int OT, int D, int G, bool PH>
 __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   constexpr int KB = Enc<KV>::bytes;
   constexpr int QB = Enc<QT>::bytes;
@@ -481,6 +483,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   float m[HPL], lsum[HPL];                 // vector-ALU path: per head of the lane's rows
   float acc[G][VEPC];                      // vector-ALU P.V: lane (r, c), all G heads
   float m1 = 0.0f, l1 = 0.0f;              // matrix-core path: head n % G, partial l
+  float qks = a.qk_scale_log2;             // score scale of the piece's kv head (log2 units)
   f32x4 acc4[DPL];                         // matrix-core P.V: dim DPL*n + e, rows 4kq + v
   bool piece_whole_start = false;          // the current piece began at its segment's start
   int piece_slot = 0;
@@ -525,6 +528,8 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       }
       piece_whole_start = (fl & kSegStart) != 0;
       piece_slot = (fl & kAtStart) ? 0 : 1;
+      // per-head dequantisation: kv head g's K codes times k_head_scales[g]
+      if constexpr (PH) qks = (a.qk_scale * a.k_head_scales[g]) * kLog2e;
     }
     const int rem = mu.rem();              // tokens of this block below L
     const bool ragged = rem < kBlockTokens;
@@ -537,7 +542,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       float sv[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sv[v] = sc[v] * a.qk_scale_log2;
+        sv[v] = sc[v] * qks;
         if (ragged) sv[v] = 4 * kq + v < rem ? sv[v] : neg_inf();
       }
       // new running max of head n % G: over the lane's 4 tokens and the running max, then
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       float al[HPL], p[HPL], sv[HPL], mn[HPL];
 #pragma unroll
       for (int r = 0; r < HPL; ++r) {
-        sv[r] = tok_ok ? sc[r] * a.qk_scale_log2 : neg_inf();
+        sv[r] = tok_ok ? sc[r] * qks : neg_inf();
         mn[r] = sv[r] > m[r] ? sv[r] : m[r];   // m is the same on all lanes of a row
       }
       row16_max_n<HPL>(mn);                  // new running maxima, one per head
@@ -656,6 +661,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     // ---- the piece ends here: reduce over lanes, then write the output (whole segment)
     // or a record (a piece of a segment cut by a chunk boundary)
     const bool whole = piece_whole_start && (fl & kSegEnd);
+    const float vsc = PH ? a.v_head_scales[g] : a.v_scale;
     const size_t rec = ((size_t)mu.chunk() * 2 + piece_slot) * NW + wave;
     if constexpr (MPV) {
       // l of head n % G over the whole block (the row groups held partial sums); lanes of
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
           const int h = hb + v;
           if (whole) {
             const size_t o = ((size_t)mu.b() * Hq + (size_t)g * G + h) * D + DPL * n;
-            const float inv = lsum[v] > 0.0f ? a.v_scale / lsum[v] : 0.0f;
+            const float inv = lsum[v] > 0.0f ? vsc / lsum[v] : 0.0f;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) store_out<OT>(a.out, o + e, acc4[e][v] * inv);
           } else {
@@ -715,7 +721,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const size_t o = ((size_t)mu.b() * Hq + (size_t)g * G + h) * D + VEPC * lane;
-            const float inv = lh[h] > 0.0f ? a.v_scale / lh[h] : 0.0f;
+            const float inv = lh[h] > 0.0f ? vsc / lh[h] : 0.0f;
 #pragma unroll
             for (int e = 0; e < VEPC; ++e) store_out<OT>(a.out, o + e, acc[h][e] * inv);
           }
@@ -795,7 +801,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Combine the pieces of segments cut by chunk boundaries, with the same rescaling:
-// M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), with
+// v_scale the per-tensor scale or kv head g's own.
 // Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
 // waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
 // query head h. Wave w folds pieces w, w + MW, ... into a running (M, L, A) with the
@@ -883,14 +890,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) At[e] = fmaf(s_acc[w][h * D + d0 + e], f, At[e]);
   }
-  const float inv = Lt > 0.0f ? a.v_scale / Lt : 0.0f;
+  const float vsc = a.v_head_scales ? a.v_head_scales[g] : a.v_scale;
+  const float inv = Lt > 0.0f ? vsc / Lt : 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, At[i] * inv);
 }
 
 template <int KV, int QT, int OT, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& args, int nw, hipStream_t stream) {
-  decode_kernel<KV, QT, OT, D, G><<<dim3(args.num_ranges), dim3(nw * kWave), 0, stream>>>(args);
+  const dim3 grid(args.num_ranges), block(nw * kWave);
+  if constexpr (KV == PA_FP8_E4M3) {
+    if (args.k_head_scales) {
+      decode_kernel<KV, QT, OT, D, G, true><<<grid, block, 0, stream>>>(args);
+      return hipGetLastError();
+    }
+  }
+  decode_kernel<KV, QT, OT, D, G, false><<<grid, block, 0, stream>>>(args);
   return hipGetLastError();
 }
 

@@ -78,8 +78,11 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t num_ranges;           // W, workgroups
   int32_t part_units;           // fixed chunk length in units, 0 = default split
-  float qk_scale_log2;          // scale * k_scale * log2(e)
+  float qk_scale_log2;          // scale * k_scale * log2(e), per-tensor scales
   float v_scale;
+  const float* k_head_scales;   // [Hkv] per-head dequantisation scales, or null (per tensor):
+  const float* v_head_scales;   //   kv head g then uses (qk_scale * k_head_scales[g]) * log2(e)
+  float qk_scale;               // scale, for the per-head path
 };
 
 // Arguments of the merge kernel: one wave per (kv head, sequence).
@@ -95,6 +98,7 @@ struct MergeArgs {
   int32_t num_ranges;           // W
   int32_t part_units;
   float v_scale;
+  const float* v_head_scales;   // [Hkv] or null
 };
 
 // Multi-token queries (pa_prefill). A workgroup of kPrefillWaves waves owns one
@@ -121,9 +125,15 @@ struct PrefillArgs {
   int32_t max_query_len;        // rows past it in a sequence are not computed
   int32_t num_q_tiles;          // query tiles per (sequence, kv head)
   int32_t num_workgroups;       // ceil(B * Hkv / 8) * num_q_tiles * 8
-  float qk_scale_log2;          // scale * k_scale * log2(e)
+  float qk_scale_log2;          // scale * k_scale * log2(e), per-tensor scales
   float v_scale;
+  const float* k_head_scales;   // [Hkv] or null: kv head g then uses
+  const float* v_head_scales;   //   (qk_scale * k_head_scales[g]) * log2(e)
+  float qk_scale;               // scale, for the per-head path
 };
+
+// log2(e) as a binary32 constant: host and kernels form score scales with it in the same order
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Waves per workgroup for Hkv kv heads: the largest of 8, 4, 2, 1 dividing Hkv.
 inline int group_waves(int num_kv_heads) {
@@ -147,7 +157,8 @@ hipError_t launch_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new,
                                   const void* v_new, const int64_t* slot_mapping,
                                   int32_t num_tokens, int32_t row_elems, int64_t num_slots,
                                   int32_t src_dtype, float k_inv, float v_inv,
-                                  hipStream_t stream);
+                                  const float* k_head_scales, const float* v_head_scales,
+                                  int32_t head_dim, hipStream_t stream);
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int64_t* pairs,
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream);

@@ -160,6 +160,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int li = lane & 15, lk = lane >> 4;
   const int Hq = a.num_q_heads;
+  // score scale and output scale of this kv head (per-head dequantisation scales if given)
+  const float qks =
+      a.k_head_scales ? (a.qk_scale * a.k_head_scales[kvh]) * kLog2e : a.qk_scale_log2;
+  const float vsc = a.v_head_scales ? a.v_head_scales[kvh] : a.v_scale;
 
   // ---- q rows as the B operand: lane (li, lk) holds dims 32c + 8lk .. +7 of row li
   u32x4 qop[RG][NC];
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float x = sc[rg][s][v] * a.qk_scale_log2;
+          float x = sc[rg][s][v] * qks;
           if constexpr (MASKED)
             x = kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] ? x : neg_inf();
           sv[s][v] = x;
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       const int r = (wave * RG + rg) * 16 + 4 * lk + v;
       const int t = t0 + r / G, h = r % G;
       if (t >= nr) continue;
-      const float inv = lr > 0.0f ? a.v_scale / lr : 0.0f;
+      const float inv = lr > 0.0f ? vsc / lr : 0.0f;
       float o[DPL];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) o[e] = acc[rg][e][v] * inv;

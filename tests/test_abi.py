@@ -194,3 +194,26 @@ def test_block_swap_rejects_before_launch(lib):
               None) == -6
     assert sw(p, p, 10, p, p, 10, ctypes.c_void_p(0x10004), 1, 8, 128, 16, pa.PA_BF16,
               None) == -6
+
+
+def test_head_scale_entry_points_reject_before_launch(lib):
+    p = ctypes.c_void_p(0x10000)
+    z = ctypes.c_void_p(0)
+    odd = ctypes.c_void_p(0x10002)
+    d = _desc(kv_dtype=pa.PA_FP8_E4M3)
+    dec = lambda ks, vs, d=d: lib.pa_decode_head_scales(  # noqa: E731
+        ctypes.byref(d), p, p, p, p, p, p, 8192, 0.088, ks, vs, p, 1 << 30, None)
+    assert dec(z, p) == -1 and dec(p, z) == -1
+    assert dec(odd, p) == -6
+    assert dec(p, p, d=_desc()) == -4               # per-head decode: fp8 pools only
+    assert lib.pa_decode_head_scales(ctypes.byref(_desc(batch=0, kv_dtype=pa.PA_FP8_E4M3)), p, p,
+                                     p, p, p, p, 8192, 0.088, z, z, None, 0, None) == 0
+    pd = _pdesc()
+    pre = lambda ks, vs: lib.pa_prefill_head_scales(ctypes.byref(pd), p, p, p, p, p, p, p, 512,  # noqa
+                                                    0.088, ks, vs, None)
+    assert pre(z, p) == -1 and pre(p, odd) == -6
+    w8 = lambda ks, vs, n=4, d=128: lib.pa_cache_write_fp8_head_scales(  # noqa: E731
+        p, p, p, p, p, n, 8, d, 16, 100, pa.PA_BF16, ks, vs, None)
+    assert w8(z, p) == -1 and w8(p, odd) == -6
+    assert w8(p, p, d=36) == -4                     # head_dim not a multiple of 8
+    assert w8(z, z, n=0) == 0
