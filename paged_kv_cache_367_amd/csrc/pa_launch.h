@@ -104,8 +104,14 @@ struct MergeArgs {
 // Multi-token queries (pa_prefill). A workgroup of kPrefillWaves waves owns one
 // (sequence, kv head, tile of query tokens); each wave holds kPrefillRowGroups groups of
 // 16 (token, head) rows, so a tile has 16 * kPrefillWaves * kPrefillRowGroups / G tokens.
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRowGroups = 2;
+#ifndef PA_PF_WAVES
+#define PA_PF_WAVES 4
+#endif
+#ifndef PA_PF_ROWGROUPS
+#define PA_PF_ROWGROUPS 2
+#endif
+constexpr int kPrefillWaves = PA_PF_WAVES;
+constexpr int kPrefillRowGroups = PA_PF_ROWGROUPS;
 inline int prefill_tile_tokens(int group) { return 16 * kPrefillWaves * kPrefillRowGroups / group; }
 
 struct PrefillArgs {

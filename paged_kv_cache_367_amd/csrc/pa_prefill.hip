@@ -48,7 +48,11 @@ namespace pa {
 namespace {
 
 constexpr int kTileTokens = 64;                      // K/V tokens per LDS tile
+#ifndef PA_PF_LPAD
+#define PA_PF_LPAD 16                                  // LDS row padding, bytes
+#endif
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
+constexpr int kStageThreads = 256;                   // threads (4 whole waves) staging K/V
 
 // One 16x16x32 MFMA in the 16-bit type CT: acc += A * B.
 template <int CT>
@@ -110,12 +114,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr bool SPLIT = KV == PA_BF16;                // p as hi + lo bf16 parts
   constexpr int KB = Enc<KV>::bytes;
   constexpr int ROWB = D * KB;                   // pool bytes of one token row, one kv head
-  constexpr int LROW = D * 2 + 16;               // LDS bytes of one token row (16-bit, padded)
+  constexpr int LROW = D * 2 + PA_PF_LPAD;       // LDS bytes of one token row (16-bit, padded)
   constexpr int ROWS = kPrefillWaves * RG * 16;  // (token, head) rows of the workgroup
   constexpr int TQ = ROWS / G;                   // query tokens of the workgroup
   constexpr int NC = D / 32;                     // 32-dim steps of a score MFMA chain
   constexpr int DPL = D / 16;                    // output dims per lane and 16-row group
-  constexpr int LB = kBlockTokens * ROWB / kPrefillThreads;  // staged bytes per thread and block
+  constexpr int LB = kBlockTokens * ROWB / kStageThreads;  // staged bytes per thread and block
   constexpr int TPR = ROWB / LB;                 // threads per token row
   static_assert(LB == 16 || LB == 8 || LB == 4, "one load per thread and block");
   using LT = typename VChunk<LB>::type;
@@ -160,9 +164,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int li = lane & 15, lk = lane >> 4;
   const int Hq = a.num_q_heads;
-  // score scale and output scale of this kv head (per-head dequantisation scales if given)
-  const float qks =
+  // score scale and output scale of this kv head (per-head dequantisation scales if given).
+  // The softmax takes the max of the raw scores and folds the scale into the exponent's
+  // fma, which needs a scale >= 0: a negative one is moved onto q (an exact sign flip).
+  const float qks_signed =
       a.k_head_scales ? (a.qk_scale * a.k_head_scales[kvh]) * kLog2e : a.qk_scale_log2;
+  const float qks = fabsf(qks_signed);
+  const uint32_t qflip = qks_signed < 0.0f ? 0x80008000u : 0u;
   const float vsc = a.v_head_scales ? a.v_head_scales[kvh] : a.v_scale;
 
   // ---- q rows as the B operand: lane (li, lk) holds dims 32c + 8lk .. +7 of row li
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                           ((size_t)(qs0 + (ok ? t : nr - 1)) * Hq + (size_t)kvh * G + h) * D * 2;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qop[rg][c] = *reinterpret_cast<const u32x4*>(qrow + (32 * c + 8 * lk) * 2);
+      qop[rg][c] = *reinterpret_cast<const u32x4*>(qrow + (32 * c + 8 * lk) * 2) ^ qflip;
   }
   // Wait for q here, once: an empty asm that reads and redefines the registers makes the
   // compiler place that wait now, instead of waiting for every load in flight at the
@@ -204,7 +212,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const __amdgpu_buffer_rsrc_t rt =
       make_rsrc(a.block_tables + (size_t)b * a.max_blocks_per_seq, (uint32_t)nb * 4u);
   auto load_ids = [&](int kt) -> u32x4 { return buf_load16(rt, (uint32_t)kt * 16u); };
+  const bool stager = kPrefillThreads == kStageThreads || wave < kStageThreads / kWave;
   auto stage = [&](int kt, const u32x4& idv, LT (&kr)[4], LT (&vr)[4]) {
+    if (!stager) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = kt * 4 + i;
@@ -219,6 +229,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     }
   };
   auto to_lds = [&](int buf, const LT (&kr)[4], const LT (&vr)[4]) {
+    if (!stager) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = kBlockTokens * i + tid / TPR;
@@ -289,20 +300,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     u32x4 alo[SPLIT ? RG : 1][2];          // the low parts of P (bf16 K/V)
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      float sv[4][4];
+      // raw scores; the max commutes with the (non-negative) scale, rounding included
+      bool live[4][4];
       float bm = neg_inf();
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float x = sc[rg][s][v] * qks;
-          if constexpr (MASKED)
-            x = kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] ? x : neg_inf();
-          sv[s][v] = x;
-          bm = fmaxf(bm, x);
+          live[s][v] = !MASKED || kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg];
+          bm = fmaxf(bm, live[s][v] ? sc[rg][s][v] : neg_inf());
         }
-      const float mn = xrow_max(fmaxf(bm, m[rg]));
+      const float mn = xrow_max(fmaxf(bm * qks, m[rg]));
       const float base = mn == neg_inf() ? 0.0f : mn;
+      // p = 2^(s * scale - max); masked positions are 0 (also for a zero scale)
+      float sv[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sv[s][v] = fmaf(sc[rg][s][v], qks, -base);
       const float al = m[rg] == mn ? 1.0f : fast_exp2(m[rg] - base);
       float ls = 0.0f;
 #pragma unroll
@@ -312,8 +327,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int v = 0; v < 4; v += 2) {
-            const float pa = fast_exp2(sv[2 * pi + h][v] - base);
-            const float pb = fast_exp2(sv[2 * pi + h][v + 1] - base);
+            float pa = fast_exp2(sv[2 * pi + h][v]);
+            float pb = fast_exp2(sv[2 * pi + h][v + 1]);
+            if constexpr (MASKED) {
+              pa = live[2 * pi + h][v] ? pa : 0.0f;
+              pb = live[2 * pi + h][v + 1] ? pb : 0.0f;
+            }
             if constexpr (SPLIT) {
               const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb);
               w[2 * h + v / 2] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // high halves
