@@ -40,7 +40,8 @@
  *
  * Conventions: all pointers are HOST pointers; the handle is not thread-safe (one caller
  * at a time); nothing touches the GPU. Errors are pa_status_t return codes (see
- * paged_attention.h) plus the two below; a failing call changes no state.
+ * paged_attention.h) plus the three below; a failing call changes no state (except
+ * PA_ERR_NO_MEMORY).
  */
 #ifndef PA_BLOCK_MANAGER_H
 #define PA_BLOCK_MANAGER_H
@@ -53,6 +54,8 @@ extern "C" {
 
 #define PA_ERR_NO_BLOCKS (-8)    /* not enough free or evictable blocks */
 #define PA_ERR_UNKNOWN_SEQ (-9)  /* no such sequence id, or the id is already in use */
+#define PA_ERR_NO_MEMORY (-10)   /* host memory ran out inside the manager; its state is then
+                                    unspecified and the handle should only be destroyed */
 
 typedef struct pa_block_manager pa_block_manager_t;
 

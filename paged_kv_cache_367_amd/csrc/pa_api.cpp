@@ -127,6 +127,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_HIP: return "HIP runtime error at launch";
     case -8: return "not enough free or evictable KV blocks";      // pa_block_manager.h
     case -9: return "unknown sequence id, or the id is in use";   // pa_block_manager.h
+    case -10: return "host memory ran out in the block manager";  // pa_block_manager.h
     default: return "unknown status";
   }
 }
