@@ -101,8 +101,9 @@ int32_t pa_decode_max_chunks(const pa_decode_desc_t* desc, int32_t max_context_l
 /* Bytes of device workspace pa_decode needs (0 for an invalid descriptor or B = 0).
  * The workspace holds two chunk counters, for each chunk the (m, l, acc) records of the
  * at most two sequence pieces it leaves unfinished (running max m in log2 units,
- * normaliser l and unnormalised output acc[d], fp32, per kv head and query head), and
- * the per-sequence prefix sums of block counts. It must be zero-filled before its first
+ * normaliser l and unnormalised output acc[d], fp32, per kv head and query head), the
+ * per-sequence prefix sums of block counts, and per chunk a 16-byte header naming the
+ * sequence piece the merge completes there. It must be zero-filled before its first
  * use; every call leaves the counters at zero again, so later calls need no clearing. */
 size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_context_len);
 

@@ -91,9 +91,9 @@ pa_status_t check_desc(const pa_decode_desc_t* d, int32_t max_context_len) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: the two chunk counters (zero between calls), the records of cut segments,
-// then the per-sequence block prefix sums.
+// the per-sequence block prefix sums, then one 16-byte header per chunk.
 struct Workspace {
-  size_t counters, acc, ml, prefix, total;   // byte offsets and size
+  size_t counters, acc, ml, prefix, hdr, total;   // byte offsets and size
 };
 Workspace workspace_layout(const pa_decode_desc_t* d, int32_t max_context_len) {
   const size_t chunks = (size_t)max_chunks(d, max_context_len);
@@ -105,7 +105,8 @@ Workspace workspace_layout(const pa_decode_desc_t* d, int32_t max_context_len) {
   w.acc = 256;
   w.ml = w.acc + align_up(recs * d->head_dim * sizeof(float), 256);
   w.prefix = w.ml + align_up(recs * 2 * sizeof(float), 256);
-  w.total = w.prefix + align_up(((size_t)d->batch + 1) * sizeof(int32_t), 256);
+  w.hdr = w.prefix + align_up(((size_t)d->batch + 1) * sizeof(int32_t), 256);
+  w.total = w.hdr + align_up(chunks * 4 * sizeof(int32_t), 256);
   return w;
 }
 
@@ -182,6 +183,7 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
   a.rec_acc = reinterpret_cast<float*>(wsb + ws.acc);
   a.rec_ml = reinterpret_cast<float*>(wsb + ws.ml);
   a.prefix = reinterpret_cast<int32_t*>(wsb + ws.prefix);
+  a.chunk_hdr = reinterpret_cast<int32_t*>(wsb + ws.hdr);
   a.batch = desc->batch;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->num_kv_heads;
@@ -206,6 +208,7 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
   m.rec_acc = a.rec_acc;
   m.rec_ml = a.rec_ml;
   m.prefix = a.prefix;
+  m.chunk_hdr = a.chunk_hdr;
   m.batch = desc->batch;
   m.num_q_heads = desc->num_q_heads;
   m.num_kv_heads = desc->num_kv_heads;

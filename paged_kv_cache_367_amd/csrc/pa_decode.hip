@@ -353,13 +353,18 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   int cur = -1;                              // current chunk, -1 once there is none
   int wu = 0, cbeg = 0, cend = 0;
   int wb = 0, whg = 0, wj = 0, wnb = 1, wL = 0;
-  auto locate = [&](int u) {                 // largest b with HGC * pre[b] <= u
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (HGC * uni(s_pre[mid]) <= u) lo = mid;
-      else hi = mid - 1;
-    }
+  // largest b with HGC * pre[b] <= u (the sequence holding unit u: empty sequences
+  // before it share its prefix sum). The prefix sums never decrease, so the b passing the
+  // test form a prefix of [0, B): count them with two wave ballots, first over 64 evenly
+  // spaced samples, then inside the stretch the count ends in.
+  const int SPAN = (B + kWave - 1) / kWave;
+  auto locate = [&](int u) {
+    const int b1 = lane * SPAN;
+    const bool p1 = b1 < B && HGC * s_pre[b1] <= u;
+    const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(p1)) - 1;
+    const int b2 = k * SPAN + lane;
+    const bool p2 = lane < SPAN && b2 < B && HGC * s_pre[b2] <= u;
+    const int lo = uni(k * SPAN + __builtin_popcountll(__builtin_amdgcn_ballot_w64(p2)) - 1);
     wb = lo;
     wL = uni(s_lens[lo]);
     wnb = nblocks(wL);
@@ -373,6 +378,17 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   auto grab = [&]() {
     if (wave == 0 && lane == 0) grab_v = atomicInc(reinterpret_cast<unsigned*>(grab_ctr), ~0u);
   };
+  // Header of the static chunk for merge_chunk_kernel (default split only): the segment
+  // whose last piece opens the chunk, if it began in an earlier chunk. Noted at entry,
+  // written once the first loads are in flight (its divisions are then off the path to
+  // the first data).
+  int hdr_c = -1, hdr_b = -1, hdr_hg = 0, hdr_sseg = 0;
+  auto note_header = [&](int c, bool cut, int sseg) {
+    hdr_c = c;
+    hdr_b = cut ? wb : -1;
+    hdr_hg = whg;
+    hdr_sseg = sseg;
+  };
   auto enter = [&](int c) {
     cur = c;
     if (c < 0) return;
@@ -381,6 +397,10 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     wu = cbeg;
     locate(wu);
     grab();
+    if (!cg.fixed && c < W) {
+      const int sseg = HGC * uni(s_pre[wb]) + whg * wnb;
+      note_header(c, wj > 0 && sseg + wnb <= cend, sseg);
+    }
   };
   // at a chunk end: wave 0 publishes the chunk it was given, all waves take it
   auto next_chunk = [&]() {
@@ -400,8 +420,17 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   if (!cg.fixed && chunk_begin(cg, rng) < chunk_end(cg, rng)) {
     enter(rng);
   } else {
+    if (!cg.fixed) note_header(rng, false, 0);   // an empty static chunk ends no segment
     grab();
     next_chunk();
+  }
+  // default split: sequences of length 0 own no units; workgroup r writes the zero
+  // outputs of sequences r, r + W, ... (with fixed partitions the merge does)
+  if (!cg.fixed) {
+    const size_t row = (size_t)Hq * D;
+    for (int b = bid; b < B; b += W)
+      if (s_lens[b] == 0)
+        for (size_t i = tid; i < row; i += nthr) store_out<OT>(a.out, (size_t)b * row + i, 0.0f);
   }
   auto snapshot = [&]() -> UnitMeta {
     UnitMeta m;
@@ -770,6 +799,14 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     idv[u] = load_id(mi[u]);
     advance();
   }
+  if (!cg.fixed && wave == 0 && lane == 0) {
+    int4 hd = make_int4(-1, 0, 0, 0);
+    if (hdr_b >= 0) {
+      const int cf = chunk_of(cg, hdr_sseg);
+      hd = make_int4(hdr_b, hdr_hg, cf, chunk_begin(cg, cf) < hdr_sseg ? 1 : 0);
+    }
+    *reinterpret_cast<int4*>(a.chunk_hdr + 4 * hdr_c) = hd;
+  }
   // every wave sees the same chunks, so the loop ends at the same step in all of them
   for (;;) {
 #pragma unroll
@@ -896,6 +933,120 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, At[i] * inv);
 }
 
+// N consecutive floats from an address aligned to the widest of 16, 8 or 4 bytes that N
+// floats fill, as vector loads.
+template <int N>
+__device__ __forceinline__ void load_floats(const float* p, float (&x)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(p)[i];
+      x[4 * i] = v[0];
+      x[4 * i + 1] = v[1];
+      x[4 * i + 2] = v[2];
+      x[4 * i + 3] = v[3];
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const f32x2 v = reinterpret_cast<const f32x2*>(p)[i];
+      x[2 * i] = v[0];
+      x[2 * i + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = p[i];
+  }
+}
+
+// Default split: combine the pieces of the segment whose last piece opens chunk c, as
+// named by chunk c's header, with the same rescaling (v_scale per tensor or per kv head).
+// Wave w handles kv head hg * NW + w; lane i holds EPL consecutive outputs of query head
+// h. The header, chunk c's first record and chunk c - 1's last record are loaded
+// together, so a segment cut once (nearly all of them) costs one memory round trip;
+// a segment spread over more chunks loads its other pieces UNROLL at a time.
+template <int OT, int D, int G>
+__global__ __launch_bounds__(kMaxThreads) void merge_chunk_kernel(MergeArgs a) {
+  constexpr int EPL = G * D / kWave;
+  constexpr int UNROLL = 8;
+  static_assert(EPL >= 1 && D % EPL == 0, "merge layout");
+  // chunk c is merged on the XCD whose workgroup decoded it (the decode's dealing of
+  // chunks to workgroup ids), where its records and their address translations are
+  // still cached
+  const int W = a.num_ranges, bid = blockIdx.x;
+  const int c = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int NW = a.group_waves;
+  const int h = lane * EPL / D, d0 = (lane * EPL) % D;
+  auto rec_of = [&](int chunk, int slot) -> size_t {
+    return (((size_t)chunk * 2 + slot) * NW + wave) * G + h;
+  };
+  const int4 hd = *reinterpret_cast<const int4*>(a.chunk_hdr + 4 * c);
+  const int total = a.prefix[a.batch];    // needed only by segments over 3+ chunks
+  const size_t r1 = rec_of(c, 0), r0 = rec_of(c > 0 ? c - 1 : 0, 1);
+  const f32x2 ml1 = *reinterpret_cast<const f32x2*>(a.rec_ml + r1 * 2);
+  const f32x2 ml0 = *reinterpret_cast<const f32x2*>(a.rec_ml + r0 * 2);
+  float x1[EPL], x0[EPL];
+  load_floats<EPL>(a.rec_acc + r1 * D + d0, x1);
+  load_floats<EPL>(a.rec_acc + r0 * D + d0, x0);
+  // keep the record loads ahead of the header test (otherwise they are sunk below it
+  // and cost a second round trip)
+  asm volatile("" ::"v"(ml1.x), "v"(ml1.y), "v"(ml0.x), "v"(ml0.y), "s"(total));
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) asm volatile("" ::"v"(x1[e]), "v"(x0[e]));
+  const int b = hd.x;
+  if (b < 0) return;
+  const int hg = hd.y, cf = hd.z, slot_f = hd.w;
+
+  float M = neg_inf(), L = 0.0f, A[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) A[e] = 0.0f;
+  auto fold = [&](float mp, float lp, const float* x) {
+    const float Mn = fmaxf(M, mp);
+    if (Mn == neg_inf()) return;         // nothing yet
+    const float sa = M == neg_inf() ? 0.0f : fast_exp2(M - Mn);
+    const float sb = mp == neg_inf() ? 0.0f : fast_exp2(mp - Mn);
+    L = L * sa + lp * sb;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) A[e] = A[e] * sa + x[e] * sb;
+    M = Mn;
+  };
+  if (cf == c - 1 && slot_f == 1) {
+    fold(ml0.x, ml0.y, x0);
+  } else {
+    // pieces in chunks cf .. c-1 (slot slot_f in chunk cf, else 0), skipping empty
+    // chunks, which exist only when there are fewer units than chunks (T < W; then
+    // T * c fits 32 bits)
+    const int64_t T = (int64_t)(a.num_kv_heads / NW) * total;
+    const int Ts = T < W ? (int)T : 0;
+    for (int cb = cf; cb < c; cb += UNROLL) {
+      // every load is issued (a piece that is skipped reads chunk c's own record), so
+      // the UNROLL pieces cost one round trip; skipped pieces are dropped in the fold
+      f32x2 mlp[UNROLL];
+      float x[UNROLL][EPL];
+      bool ok[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int cc = cb + u;
+        ok[u] = cc < c && (Ts == 0 || Ts * cc / W < Ts * (cc + 1) / W);
+        const size_t rec = rec_of(ok[u] ? cc : c, (ok[u] && cc == cf) ? slot_f : 0);
+        mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
+        load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        if (ok[u]) fold(mlp[u].x, mlp[u].y, x[u]);
+    }
+  }
+  fold(ml1.x, ml1.y, x1);
+  const int g = hg * NW + wave;
+  const float vsc = a.v_head_scales ? a.v_head_scales[g] : a.v_scale;
+  const float inv = L > 0.0f ? vsc / L : 0.0f;
+  const size_t o = ((size_t)b * a.num_q_heads + (size_t)g * G + h) * D + d0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_out<OT>(a.out, o + e, A[e] * inv);
+}
+
 template <int KV, int QT, int OT, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& args, int nw, hipStream_t stream) {
   const dim3 grid(args.num_ranges), block(nw * kWave);
@@ -932,6 +1083,17 @@ hipError_t dispatch_dim(int head_dim, int group, const DecodeArgs& args, int nw,
 
 template <int OT, int D>
 hipError_t launch_merge_t(int group, const MergeArgs& args, hipStream_t stream) {
+  if (args.part_units == 0) {             // default split: one workgroup per chunk
+    const dim3 grid(args.num_ranges), block(args.group_waves * kWave);
+    switch (group) {
+      case 1: merge_chunk_kernel<OT, D, 1><<<grid, block, 0, stream>>>(args); break;
+      case 2: merge_chunk_kernel<OT, D, 2><<<grid, block, 0, stream>>>(args); break;
+      case 4: merge_chunk_kernel<OT, D, 4><<<grid, block, 0, stream>>>(args); break;
+      case 8: merge_chunk_kernel<OT, D, 8><<<grid, block, 0, stream>>>(args); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(args.num_kv_heads, args.batch), block(256);
   switch (group) {
     case 1: merge_kernel<OT, D, 1><<<grid, block, 0, stream>>>(args); break;

@@ -70,6 +70,9 @@ struct DecodeArgs {
   float* rec_acc;               // [chunks, 2, NW, G, d]  unnormalised partial outputs
   float* rec_ml;                // [chunks, 2, NW, G, 2]  (running max m in log2 units, sum l)
   int32_t* prefix;              // [B + 1] blocks before each sequence (workgroup 0 writes)
+  int32_t* chunk_hdr;           // [chunks][4] default split: the cut segment whose last
+                                //   piece opens the chunk (b, head group, first chunk, slot
+                                //   of its piece there), b = -1 if none
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -85,12 +88,14 @@ struct DecodeArgs {
   float qk_scale;               // scale, for the per-head path
 };
 
-// Arguments of the merge kernel: one wave per (kv head, sequence).
+// Arguments of the merge kernels: with the default split one workgroup per chunk (the
+// segment its header names), with fixed partitions one per (kv head, sequence).
 struct MergeArgs {
   void* out;
   const float* rec_acc;
   const float* rec_ml;
   const int32_t* prefix;
+  const int32_t* chunk_hdr;
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
