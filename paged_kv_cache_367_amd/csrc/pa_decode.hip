@@ -34,7 +34,9 @@
 //     used G times. At the end of a piece, lanes owning the same chunk are summed.
 //   * A sequence whose segment lies in one share is written out directly. A segment cut
 //     by share boundaries leaves one (m, l, acc) record per piece (at most two per wave:
-//     the share's first and last segment), and merge_kernel combines them.
+//     the share's first and last segment), and a merge kernel combines them
+//     (merge_chunk_kernel: one workgroup per chunk, named by a header the decode
+//     writes; with fixed partitions merge_kernel, one per (kv head, sequence)).
 //   * The partial last block is masked by selection (scores -> -inf, V -> 0), so stale
 //     or NaN slots past L never reach the result.
 //   * Reduction order depends on logical positions and lengths only, never on physical

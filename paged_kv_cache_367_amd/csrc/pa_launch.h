@@ -21,7 +21,7 @@ constexpr int kMaxBatch = 4096;       // lengths and prefix sums of the batch si
 // of nb = ceil(L / 16) units. There are T = (Hkv / NW) * sum_b nb units, cut into chunks;
 // a workgroup of NW waves (one per kv head of the group) walks its chunks unit by unit.
 // A segment cut by a chunk boundary leaves one (m, l, acc) record per piece, which
-// merge_kernel combines; a segment inside one chunk is written out directly.
+// merge kernels combine; a segment inside one chunk is written out directly.
 //
 // Chunks of [0, T), numbered in unit order. Default: W static chunks, chunk r =
 // [T*r/W, T*(r+1)/W), one per workgroup (a chunk may be empty when T < W). With a fixed
@@ -31,9 +31,12 @@ struct ChunkGeom {
   int64_t T, C2;
   int W, nsmall;
   bool fixed;
+  int q, r, wshift;   // T = q * W + r; wshift = log2(W) when W is a power of two, else -1
 };
 constexpr int64_t kMaxChunks = 16384;
 
+// T < 2^31 (the host checks unit counts) and W <= 2048, so static chunk bounds need only
+// 32-bit products, and a shift when W is a power of two (it is for every head count).
 __host__ __device__ inline ChunkGeom chunk_geometry(int64_t T, int W, int fixed_units) {
   ChunkGeom g;
   g.T = T;
@@ -41,14 +44,23 @@ __host__ __device__ inline ChunkGeom chunk_geometry(int64_t T, int W, int fixed_
   g.fixed = fixed_units > 0;
   g.C2 = g.fixed ? fixed_units : 1;
   g.nsmall = g.fixed ? (int)((T + fixed_units - 1) / fixed_units) : 0;
+  g.wshift = (W & (W - 1)) == 0 ? __builtin_ctz((unsigned)W) : -1;
+  const int Ti = (int)T;
+  g.q = g.wshift >= 0 ? Ti >> g.wshift : Ti / W;
+  g.r = Ti - g.q * W;
   return g;
 }
+// floor(T * c / W) for 0 <= c <= W
+__host__ __device__ inline int64_t static_bound(const ChunkGeom& g, int c) {
+  const int rc = g.r * c;
+  return (int64_t)g.q * c + (g.wshift >= 0 ? rc >> g.wshift : rc / g.W);
+}
 __host__ __device__ inline int64_t chunk_begin(const ChunkGeom& g, int c) {
-  if (c < g.W) return g.fixed ? 0 : g.T * c / g.W;
+  if (c < g.W) return g.fixed ? 0 : static_bound(g, c);
   return (int64_t)(c - g.W) * g.C2;
 }
 __host__ __device__ inline int64_t chunk_end(const ChunkGeom& g, int c) {
-  if (c < g.W) return g.fixed ? 0 : g.T * (c + 1) / g.W;
+  if (c < g.W) return g.fixed ? 0 : static_bound(g, c + 1);
   const int64_t e = chunk_begin(g, c) + g.C2;
   return e > g.T ? g.T : e;
 }
