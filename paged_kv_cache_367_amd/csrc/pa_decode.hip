@@ -839,102 +839,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Combine the pieces of segments cut by chunk boundaries, with the same rescaling:
-// M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), with
-// v_scale the per-tensor scale or kv head g's own.
-// Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
-// waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
-// query head h. Wave w folds pieces w, w + MW, ... into a running (M, L, A) with the
-// online rule, UNROLL pieces per memory round trip (each piece's (m, l) and partial
-// output are loaded together); the MW partial results are then combined through LDS.
-template <int OT, int D, int G>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int EPL = G * D / kWave;
-  constexpr int MW = 4, UNROLL = 4;
-  static_assert(EPL >= 1 && D % EPL == 0, "merge layout");
-  __shared__ float s_ml[MW][G][2];
-  __shared__ float s_acc[MW][G * D];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int h = lane * EPL / D, d0 = (lane * EPL) % D;
-  const size_t o = ((size_t)b * a.num_q_heads + (size_t)g * G + h) * D + d0;
-  const int c0 = a.prefix[b], nb = a.prefix[b + 1] - c0, total = a.prefix[a.batch];
-  if (nb == 0) {
-    if (wave == 0)
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, 0.0f);
-    return;
-  }
-  const int NW = a.group_waves, HGC = a.num_kv_heads / NW;
-  const int hg = g / NW, wv = g % NW;
-  const int64_t T = (int64_t)HGC * total;
-  const int64_t S = (int64_t)HGC * c0 + (int64_t)hg * nb, E = S + nb - 1;
-  const ChunkGeom cg = chunk_geometry(T, a.num_ranges, a.part_units);
-  const int cf = chunk_of(cg, S), cl = chunk_of(cg, E);
-  if (cf == cl) return;                  // one chunk held the whole segment
-  // records of chunk c: its first piece is in slot 0, its last (if different) in slot
-  // 1; only chunk cf can hold the segment as its last piece. Empty chunks left none.
-  const int slot_f = chunk_begin(cg, cf) < S ? 1 : 0;
-  auto rec_of = [&](int c) -> size_t {
-    return (((size_t)c * 2 + (c == cf ? slot_f : 0)) * NW + wv) * G + h;
-  };
-
-  float M = neg_inf(), L = 0.0f, A[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) A[i] = 0.0f;
-  for (int cb = cf + wave; cb <= cl; cb += MW * UNROLL) {
-    float mp[UNROLL], lp[UNROLL], x[UNROLL][EPL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int c = cb + u * MW;
-      const bool ok = c <= cl && chunk_begin(cg, c) < chunk_end(cg, c);
-      const size_t rec = rec_of(ok ? c : cf);
-      mp[u] = ok ? a.rec_ml[rec * 2] : neg_inf();
-      lp[u] = ok ? a.rec_ml[rec * 2 + 1] : 0.0f;
-      const float* src = a.rec_acc + rec * D + d0;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) x[u][e] = ok ? src[e] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const float Mn = fmaxf(M, mp[u]);
-      if (Mn == neg_inf()) continue;     // nothing yet
-      const float sa = M == neg_inf() ? 0.0f : fast_exp2(M - Mn);
-      const float sb = mp[u] == neg_inf() ? 0.0f : fast_exp2(mp[u] - Mn);
-      L = L * sa + lp[u] * sb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) A[e] = A[e] * sa + x[u][e] * sb;
-      M = Mn;
-    }
-  }
-  if (d0 == 0) {
-    s_ml[wave][h][0] = M;
-    s_ml[wave][h][1] = L;
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) s_acc[wave][h * D + d0 + e] = A[e];
-  __syncthreads();
-  if (wave != 0) return;
-  float Mt = neg_inf();
-#pragma unroll
-  for (int w = 0; w < MW; ++w) Mt = fmaxf(Mt, s_ml[w][h][0]);
-  float Lt = 0.0f, At[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) At[e] = 0.0f;
-#pragma unroll
-  for (int w = 0; w < MW; ++w) {
-    const float mw = s_ml[w][h][0];
-    const float f = mw == neg_inf() ? 0.0f : fast_exp2(mw - Mt);
-    Lt = fmaf(s_ml[w][h][1], f, Lt);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) At[e] = fmaf(s_acc[w][h * D + d0 + e], f, At[e]);
-  }
-  const float vsc = a.v_head_scales ? a.v_head_scales[g] : a.v_scale;
-  const float inv = Lt > 0.0f ? vsc / Lt : 0.0f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, At[i] * inv);
-}
-
 // N consecutive floats from an address aligned to the widest of 16, 8 or 4 bytes that N
 // floats fill, as vector loads.
 template <int N>
@@ -959,6 +863,110 @@ __device__ __forceinline__ void load_floats(const float* p, float (&x)[N]) {
 #pragma unroll
     for (int i = 0; i < N; ++i) x[i] = p[i];
   }
+}
+
+// Fixed partitions: combine the pieces of segments cut by chunk boundaries, with the
+// same rescaling: M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p
+// l_p 2^(m_p - M), with v_scale the per-tensor scale or kv head g's own.
+// Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
+// waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
+// query head h. Wave w folds pieces w, w + MW, ... into a running (M, L, A) with the
+// online rule, UNROLL pieces per memory round trip (all of a 32k-token sequence's
+// 512-token partitions in one trip); the MW partial results are then combined through
+// LDS.
+// waves of a fixed-partition merge workgroup: 16, or 8 when G * D = 1024 (the partial
+// results then still fit 32 KB of LDS)
+template <int G, int D>
+constexpr int merge_waves() { return G * D >= 1024 ? 8 : 16; }
+
+template <int OT, int D, int G>
+__global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
+  constexpr int EPL = G * D / kWave;
+  constexpr int MW = merge_waves<G, D>(), UNROLL = 4;
+  static_assert(EPL >= 1 && D % EPL == 0, "merge layout");
+  __shared__ float s_ml[MW][G][2];
+  __shared__ float s_acc[MW][G * D];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int h = lane * EPL / D, d0 = (lane * EPL) % D;
+  const size_t o = ((size_t)b * a.num_q_heads + (size_t)g * G + h) * D + d0;
+  const int c0 = a.prefix[b], nb = a.prefix[b + 1] - c0, total = a.prefix[a.batch];
+  if (nb == 0) {
+    if (wave == 0)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, 0.0f);
+    return;
+  }
+  const int NW = a.group_waves, HGC = a.num_kv_heads / NW;
+  const int hg = g / NW, wv = g % NW;
+  const int64_t T = (int64_t)HGC * total;
+  const int64_t S = (int64_t)HGC * c0 + (int64_t)hg * nb, E = S + nb - 1;
+  const ChunkGeom cg = chunk_geometry(T, a.num_ranges, a.part_units);
+  // small chunks: W + u / P, with u < 2^31 and P < 2^16
+  const int P = (int)cg.C2;
+  const int cf = cg.W + (int)S / P, cl = cg.W + (int)E / P;
+  if (cf == cl) return;                  // one chunk held the whole segment
+  // records of chunk c: its first piece is in slot 0, its last (if different) in slot
+  // 1; only chunk cf can hold the segment as its last piece. Every small chunk is
+  // non-empty.
+  const int slot_f = chunk_begin(cg, cf) < S ? 1 : 0;
+  auto rec_of = [&](int c) -> size_t {
+    return (((size_t)c * 2 + (c == cf ? slot_f : 0)) * NW + wv) * G + h;
+  };
+
+  float M = neg_inf(), L = 0.0f, A[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) A[i] = 0.0f;
+  for (int cb = cf + wave; cb <= cl; cb += MW * UNROLL) {
+    // every load is issued (a piece past cl reads chunk cf's record and is dropped)
+    f32x2 mlp[UNROLL];
+    float x[UNROLL][EPL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int c = cb + u * MW;
+      const size_t rec = rec_of(c <= cl ? c : cf);
+      mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
+      load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (cb + u * MW > cl) continue;
+      const float Mn = fmaxf(M, mlp[u].x);
+      if (Mn == neg_inf()) continue;     // nothing yet
+      const float sa = M == neg_inf() ? 0.0f : fast_exp2(M - Mn);
+      const float sb = mlp[u].x == neg_inf() ? 0.0f : fast_exp2(mlp[u].x - Mn);
+      L = L * sa + mlp[u].y * sb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) A[e] = A[e] * sa + x[u][e] * sb;
+      M = Mn;
+    }
+  }
+  if (d0 == 0) {
+    s_ml[wave][h][0] = M;
+    s_ml[wave][h][1] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_acc[wave][h * D + d0 + e] = A[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = neg_inf();
+#pragma unroll
+  for (int w = 0; w < MW; ++w) Mt = fmaxf(Mt, s_ml[w][h][0]);
+  float Lt = 0.0f, At[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) At[e] = 0.0f;
+#pragma unroll 2
+  for (int w = 0; w < MW; ++w) {
+    const float mw = s_ml[w][h][0];
+    const float f = mw == neg_inf() ? 0.0f : fast_exp2(mw - Mt);
+    Lt = fmaf(s_ml[w][h][1], f, Lt);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) At[e] = fmaf(s_acc[w][h * D + d0 + e], f, At[e]);
+  }
+  const float vsc = a.v_head_scales ? a.v_head_scales[g] : a.v_scale;
+  const float inv = Lt > 0.0f ? vsc / Lt : 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) store_out<OT>(a.out, o + i, At[i] * inv);
 }
 
 // Default split: combine the pieces of the segment whose last piece opens chunk c, as
@@ -1096,12 +1104,12 @@ hipError_t launch_merge_t(int group, const MergeArgs& args, hipStream_t stream) 
     }
     return hipGetLastError();
   }
-  const dim3 grid(args.num_kv_heads, args.batch), block(256);
+  const dim3 grid(args.num_kv_heads, args.batch);
   switch (group) {
-    case 1: merge_kernel<OT, D, 1><<<grid, block, 0, stream>>>(args); break;
-    case 2: merge_kernel<OT, D, 2><<<grid, block, 0, stream>>>(args); break;
-    case 4: merge_kernel<OT, D, 4><<<grid, block, 0, stream>>>(args); break;
-    case 8: merge_kernel<OT, D, 8><<<grid, block, 0, stream>>>(args); break;
+    case 1: merge_kernel<OT, D, 1><<<grid, merge_waves<1, D>() * kWave, 0, stream>>>(args); break;
+    case 2: merge_kernel<OT, D, 2><<<grid, merge_waves<2, D>() * kWave, 0, stream>>>(args); break;
+    case 4: merge_kernel<OT, D, 4><<<grid, merge_waves<4, D>() * kWave, 0, stream>>>(args); break;
+    case 8: merge_kernel<OT, D, 8><<<grid, merge_waves<8, D>() * kWave, 0, stream>>>(args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
