@@ -1,0 +1,73 @@
+"""Parity of the default split's cut-segment merge at engineered chunk boundaries.
+
+With 8 kv heads per workgroup the decode deals T units (16-token blocks of a sequence,
+per head group) into W = 256 static chunks [T*r/W, T*(r+1)/W). Choosing the block counts
+makes the chunk boundaries fall exactly where the merge's cases differ: a segment that
+begins exactly at a chunk boundary and ends in the next chunk, segments that are exactly
+one or two chunks, segments over many chunks with empty chunks among them (T < W), zero
+lengths in between, and two head groups per sequence. Every output is compared with the
+oracle (max-abs error 1e-2 for bf16).
+"""
+import numpy as np
+import pytest
+
+import workload as wl
+from tests.gpu_harness import TOL, as_f64, gpu_decode, max_abs_err, oracle_decode, to_device
+
+pytestmark = pytest.mark.gpu
+
+W = 256   # static chunks for 8 kv heads per workgroup (8 waves per CU on 256 CUs)
+
+
+def _lengths(blocks, seed):
+    """Context lengths with exactly the given block counts, ragged inside the last block."""
+    rng = np.random.default_rng(seed)
+    nb = np.asarray(blocks, dtype=np.int64)
+    tail = rng.integers(1, 17, size=nb.size)
+    return np.where(nb > 0, (nb - 1) * 16 + tail, 0)
+
+
+def _run(blocks, num_kv_heads=8, num_q_heads=32, seed=0):
+    L = _lengths(blocks, seed)
+    w = wl.custom(batch=L.size, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                  head_dim=128, kv_dtype="bf16", context_lens=L, seed=seed)
+    out = as_f64(gpu_decode(w, to_device(w)))
+    err = max_abs_err(out, oracle_decode(w))
+    assert err <= TOL["bf16"], err
+    return w
+
+
+def test_segment_starting_at_a_chunk_boundary_ends_in_the_next():
+    # blocks 6, 2, 6, 2, ...: T = 1024, chunks of 4 units; each 6-block sequence starts a
+    # chunk and ends two units into the next one
+    blocks = [6, 2] * 128
+    assert sum(blocks) == 4 * W
+    _run(blocks)
+
+
+def test_segments_of_exactly_one_and_two_chunks():
+    _run([4] * 256)                      # every sequence is one whole chunk: nothing cut
+    _run([8] * 128, seed=1)              # every sequence is exactly two chunks
+
+
+def test_segments_over_many_chunks_with_empty_chunks_and_zero_lengths():
+    # T = 255 < W: one static chunk is empty; the 100-block sequence spans 100 chunks
+    blocks = [100, 0, 50, 60, 0, 30, 10, 5]
+    assert sum(blocks) == W - 1
+    _run(blocks, seed=2)
+
+
+def test_long_segments_spanning_several_chunks():
+    # T = 2048 (chunks of 8 units); sequences of 3..40 blocks cut once or many times
+    rng = np.random.default_rng(3)
+    blocks = list(rng.integers(3, 41, size=90))
+    blocks.append(2048 - sum(blocks))
+    assert blocks[-1] > 0
+    _run(blocks, seed=3)
+
+
+def test_two_head_groups_per_sequence():
+    # 16 kv heads: two head groups, so a sequence is two segments of nb units each
+    blocks = [6, 2] * 64
+    assert 2 * sum(blocks) == 4 * W
+    _run(blocks, num_kv_heads=16, num_q_heads=32, seed=4)
