@@ -12,8 +12,11 @@ step never finds the previous step's KV in the 256 MB Infinity Cache or the L2s.
 Output: one JSON line on stdout. `value` is KV-read GB/s over the whole step
 (sum_b L_b * 2 * Hkv * d * bytes / step time); `tokens_per_s` is sequences (one new
 token each) per second for this one attention layer. `roofline` describes the decode
-launch (main + merge kernels), timed with HIP events on the stream it runs on.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+launch (main + merge kernels), timed with HIP events on the stream it runs on (mean, and
+p10/p50/p90 over the timed steps), and sets its bandwidth against the 8 TB/s peak and
+against a copy ceiling measured on the same GPU after the timed region (a 1 GiB device
+copy, bytes read plus written). `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload.
 
 With --path prefill the step is one chunked-prefill step instead (workload.chunked_prefill:
 16 prompts x 512 new tokens over contexts of up to 8192): the slot write of the chunk's
@@ -79,6 +82,26 @@ def read_traffic(config_name: str):
         return None
     m = re.search(rf"traffic_bytes_per_launch\[{re.escape(config_name)}\]:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
+
+
+def copy_ceiling_gbs(mib: int = 1024, reps: int = 5) -> float:
+    """Measured HBM ceiling on this GPU: a device-to-device copy of `mib` MiB (torch's
+    copy kernel), bytes read plus bytes written per second, best of `reps`."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * n / (best * 1e-3) / 1e9
 
 
 def cpu_baseline(w, gpu_out, k_after, v_after, budget_s: float):
@@ -499,6 +522,9 @@ def main() -> int:
     ms = start.elapsed_time(end) / args.steps
     dec_ms = [a.elapsed_time(b) for a, b in zip(dec0, dec1)]
     dec_avg = sum(dec_ms) / len(dec_ms)
+    dec_sorted = sorted(dec_ms)
+    pct = lambda f: dec_sorted[min(len(dec_sorted) - 1, int(f * len(dec_sorted)))]
+    copy_gbs = copy_ceiling_gbs()
     log(f"timed {args.steps} steps: {ms:.4f} ms/step, decode launch avg {dec_avg:.4f} ms "
         f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f})")
 
@@ -521,10 +547,13 @@ def main() -> int:
         "tokens_per_s": w.batch / (ms * 1e-3),
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "roofline": {
-            "kernel": "pa_decode (decode_kernel + merge_kernel)", "bound": "hbm",
+            "kernel": "pa_decode (decode_kernel + %s)"
+                      % ("merge_kernel" if part else "merge_chunk_kernel"), "bound": "hbm",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
             "launch_ms": dec_avg, "algorithmic_bytes_per_launch": w.kv_bytes,
+            "launch_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+            "copy_ceiling_gbs": copy_gbs, "frac_of_copy_ceiling": achieved / copy_gbs,
         },
         "cpu_baseline": None,
     }
