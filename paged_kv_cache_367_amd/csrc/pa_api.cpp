@@ -215,6 +215,15 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
   m.group_waves = nw;
   m.num_ranges = W;
   m.part_units = a.part_units;
+  // default split: the per-chunk merge (one round trip for a segment cut once) when a call
+  // can have at least 8 units per chunk; with fewer, a segment may be cut into many pieces
+  // and the per-(kv head, sequence) merge folds 64 of them per round trip
+  {
+    const int64_t seq_blocks =
+        ((int64_t)max_context_len + pa::kBlockTokens - 1) / pa::kBlockTokens;
+    const int64_t max_units = (int64_t)(desc->num_kv_heads / nw) * desc->batch * seq_blocks;
+    m.chunk_merge = max_units >= 8 * (int64_t)W ? 1 : 0;
+  }
   m.v_scale = v_scale;
   m.v_head_scales = v_heads;
   if (pa::launch_merge(desc->out_dtype, desc->head_dim, group, m, s) != hipSuccess)

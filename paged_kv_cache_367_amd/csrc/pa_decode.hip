@@ -865,8 +865,9 @@ __device__ __forceinline__ void load_floats(const float* p, float (&x)[N]) {
   }
 }
 
-// Fixed partitions: combine the pieces of segments cut by chunk boundaries, with the
-// same rescaling: M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p
+// Fixed partitions, and the default split when a call can have few units per chunk (so
+// that a segment may be cut into many pieces): combine the pieces of segments cut by
+// chunk boundaries, with the same rescaling: M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p
 // l_p 2^(m_p - M), with v_scale the per-tensor scale or kv head g's own.
 // Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
 // waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
@@ -902,35 +903,51 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
   const int64_t T = (int64_t)HGC * total;
   const int64_t S = (int64_t)HGC * c0 + (int64_t)hg * nb, E = S + nb - 1;
   const ChunkGeom cg = chunk_geometry(T, a.num_ranges, a.part_units);
-  // small chunks: W + u / P, with u < 2^31 and P < 2^16
-  const int P = (int)cg.C2;
-  const int cf = cg.W + (int)S / P, cl = cg.W + (int)E / P;
-  if (cf == cl) return;                  // one chunk held the whole segment
+  const int W = cg.W;
+  // The segment's pieces, in unit order: with fixed partitions small chunks W + u / P
+  // (u < 2^31, P < 2^16), all non-empty; with the default split, static chunks, which
+  // hold at most one unit each when T < W (then a piece per unit, in chunk
+  // ((u + 1) W - 1) / T, so the empty chunks between them are never visited).
+  const bool by_unit = !cg.fixed && T < W;
+  const int Ti = (int)T, Si = (int)S, Ei = (int)E;
+  int cf, np;
+  if (cg.fixed) {
+    const int P = (int)cg.C2;
+    cf = W + Si / P;
+    np = W + Ei / P - cf + 1;
+  } else if (by_unit) {
+    cf = ((Si + 1) * W - 1) / Ti;
+    np = Ei - Si + 1;
+  } else {
+    cf = chunk_of(cg, S);
+    np = chunk_of(cg, E) - cf + 1;
+  }
+  if (np == 1) return;                   // one chunk held the whole segment
   // records of chunk c: its first piece is in slot 0, its last (if different) in slot
-  // 1; only chunk cf can hold the segment as its last piece. Every small chunk is
-  // non-empty.
+  // 1; only chunk cf can hold the segment as its last piece
   const int slot_f = chunk_begin(cg, cf) < S ? 1 : 0;
-  auto rec_of = [&](int c) -> size_t {
-    return (((size_t)c * 2 + (c == cf ? slot_f : 0)) * NW + wv) * G + h;
+  auto rec_of = [&](int k) -> size_t {   // piece k of the segment
+    const int c = by_unit ? ((Si + k + 1) * W - 1) / Ti : cf + k;
+    return (((size_t)c * 2 + (k == 0 ? slot_f : 0)) * NW + wv) * G + h;
   };
 
   float M = neg_inf(), L = 0.0f, A[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) A[i] = 0.0f;
-  for (int cb = cf + wave; cb <= cl; cb += MW * UNROLL) {
-    // every load is issued (a piece past cl reads chunk cf's record and is dropped)
+  for (int kb = wave; kb < np; kb += MW * UNROLL) {
+    // every load is issued (a piece past the last reads piece 0's record and is dropped)
     f32x2 mlp[UNROLL];
     float x[UNROLL][EPL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int c = cb + u * MW;
-      const size_t rec = rec_of(c <= cl ? c : cf);
+      const int k = kb + u * MW;
+      const size_t rec = rec_of(k < np ? k : 0);
       mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
       load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      if (cb + u * MW > cl) continue;
+      if (kb + u * MW >= np) continue;
       const float Mn = fmaxf(M, mlp[u].x);
       if (Mn == neg_inf()) continue;     // nothing yet
       const float sa = M == neg_inf() ? 0.0f : fast_exp2(M - Mn);
@@ -1024,28 +1041,30 @@ __global__ __launch_bounds__(kMaxThreads) void merge_chunk_kernel(MergeArgs a) {
   if (cf == c - 1 && slot_f == 1) {
     fold(ml0.x, ml0.y, x0);
   } else {
-    // pieces in chunks cf .. c-1 (slot slot_f in chunk cf, else 0), skipping empty
-    // chunks, which exist only when there are fewer units than chunks (T < W; then
-    // T * c fits 32 bits)
+    // pieces in chunks cf .. c-1 (slot slot_f in chunk cf, else 0). Static chunks are
+    // empty only when there are fewer units than chunks (T < W); each then holds at most
+    // one unit, so the pieces are the segment's units before chunk c's, unit u in chunk
+    // ((u + 1) W - 1) / T (32-bit: T < W <= 2048).
     const int64_t T = (int64_t)(a.num_kv_heads / NW) * total;
     const int Ts = T < W ? (int)T : 0;
-    for (int cb = cf; cb < c; cb += UNROLL) {
-      // every load is issued (a piece that is skipped reads chunk c's own record), so
-      // the UNROLL pieces cost one round trip; skipped pieces are dropped in the fold
+    const int u0 = Ts > 0 ? Ts * cf / W : 0;             // the segment's first unit
+    const int n = Ts > 0 ? Ts * c / W - u0 : c - cf;     // pieces before chunk c
+    for (int kb = 0; kb < n; kb += UNROLL) {
+      // every load is issued (a piece past the last reads chunk c's own record), so
+      // the UNROLL pieces cost one round trip; those past the last are dropped
       f32x2 mlp[UNROLL];
       float x[UNROLL][EPL];
-      bool ok[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int cc = cb + u;
-        ok[u] = cc < c && (Ts == 0 || Ts * cc / W < Ts * (cc + 1) / W);
-        const size_t rec = rec_of(ok[u] ? cc : c, (ok[u] && cc == cf) ? slot_f : 0);
+        const int k = kb + u;
+        const int cc = k >= n ? c : Ts > 0 ? ((u0 + k + 1) * W - 1) / Ts : cf + k;
+        const size_t rec = rec_of(cc, (k == 0) ? slot_f : 0);
         mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
         load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        if (ok[u]) fold(mlp[u].x, mlp[u].y, x[u]);
+        if (kb + u < n) fold(mlp[u].x, mlp[u].y, x[u]);
     }
   }
   fold(ml1.x, ml1.y, x1);
@@ -1093,7 +1112,7 @@ hipError_t dispatch_dim(int head_dim, int group, const DecodeArgs& args, int nw,
 
 template <int OT, int D>
 hipError_t launch_merge_t(int group, const MergeArgs& args, hipStream_t stream) {
-  if (args.part_units == 0) {             // default split: one workgroup per chunk
+  if (args.part_units == 0 && args.chunk_merge) {   // one workgroup per chunk
     const dim3 grid(args.num_ranges), block(args.group_waves * kWave);
     switch (group) {
       case 1: merge_chunk_kernel<OT, D, 1><<<grid, block, 0, stream>>>(args); break;

@@ -28,12 +28,25 @@ def _lengths(blocks, seed):
 
 
 def _run(blocks, num_kv_heads=8, num_q_heads=32, seed=0):
+    """Decode the workload twice: with its own table width, and with the tables padded
+    (-1) so wide that a call could have 8 units per chunk, which selects the per-chunk
+    merge; smaller bounds select the per-(kv head, sequence) merge."""
+    import torch
     L = _lengths(blocks, seed)
     w = wl.custom(batch=L.size, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                   head_dim=128, kv_dtype="bf16", context_lens=L, seed=seed)
-    out = as_f64(gpu_decode(w, to_device(w)))
-    err = max_abs_err(out, oracle_decode(w))
-    assert err <= TOL["bf16"], err
+    ref = oracle_decode(w)
+    d = to_device(w)
+    groups = num_kv_heads // 8
+    width = max(w.block_tables.shape[1], -(-8 * W // (groups * L.size)))
+    wide = np.full((L.size, width), -1, dtype=np.int32)
+    wide[:, :w.block_tables.shape[1]] = w.block_tables
+    for tables, max_len in ((d["tables"], w.max_context_len),
+                            (torch.from_numpy(wide).cuda(), 16 * width)):
+        dd = dict(d, tables=tables)
+        out = as_f64(gpu_decode(w, dd, max_context_len=max_len))
+        err = max_abs_err(out, ref)
+        assert err <= TOL["bf16"], (max_len, err)
     return w
 
 
@@ -71,3 +84,10 @@ def test_two_head_groups_per_sequence():
     blocks = [6, 2] * 64
     assert 2 * sum(blocks) == 4 * W
     _run(blocks, num_kv_heads=16, num_q_heads=32, seed=4)
+
+
+@pytest.mark.parametrize("L", [4096, 8191, 300])
+def test_single_long_sequence(L):
+    # batch 1: the sequence's blocks are spread over every chunk (one unit per chunk for
+    # 4096 tokens), so its merge folds up to 256 pieces
+    _run([-(-L // 16)], seed=5)
