@@ -867,8 +867,9 @@ __device__ __forceinline__ void load_floats(const float* p, float (&x)[N]) {
 
 // Fixed partitions, and the default split when a call can have few units per chunk (so
 // that a segment may be cut into many pieces): combine the pieces of segments cut by
-// chunk boundaries, with the same rescaling: M = max_p m_p, out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p
-// l_p 2^(m_p - M), with v_scale the per-tensor scale or kv head g's own.
+// chunk boundaries, with the same rescaling: M = max_p m_p,
+// out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), with v_scale the
+// per-tensor scale or kv head g's own.
 // Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
 // waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
 // query head h. Wave w folds pieces w, w + MW, ... into a running (M, L, A) with the
