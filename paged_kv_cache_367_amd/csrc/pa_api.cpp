@@ -223,6 +223,11 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
         ((int64_t)max_context_len + pa::kBlockTokens - 1) / pa::kBlockTokens;
     const int64_t max_units = (int64_t)(desc->num_kv_heads / nw) * desc->batch * seq_blocks;
     m.chunk_merge = max_units >= 8 * (int64_t)W ? 1 : 0;
+    // a segment holds at most seq_blocks units: one piece per partition (plus one when
+    // unaligned), or with the default split one per unit at most
+    const int pu = part_units(desc);
+    const int64_t pieces = pu > 0 ? (seq_blocks + pu - 1) / pu + 1 : seq_blocks;
+    m.max_pieces = (int32_t)(pieces < INT32_MAX ? pieces : INT32_MAX);
   }
   m.v_scale = v_scale;
   m.v_head_scales = v_heads;

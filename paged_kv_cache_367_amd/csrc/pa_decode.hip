@@ -884,10 +884,11 @@ constexpr int merge_waves() { return G * D >= 1024 ? 8 : 16; }
 template <int OT, int D, int G>
 __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
   constexpr int EPL = G * D / kWave;
-  constexpr int MW = merge_waves<G, D>(), UNROLL = 4;
+  constexpr int MWMAX = merge_waves<G, D>(), UNROLL = 4;
   static_assert(EPL >= 1 && D % EPL == 0, "merge layout");
-  __shared__ float s_ml[MW][G][2];
-  __shared__ float s_acc[MW][G * D];
+  __shared__ float s_ml[MWMAX][G][2];
+  __shared__ float s_acc[MWMAX][G * D];
+  const int MW = blockDim.x / kWave;       // 4, or MWMAX when a segment may have > 16 pieces
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int g = blockIdx.x, b = blockIdx.y;
   const int h = lane * EPL / D, d0 = (lane * EPL) % D;
@@ -1124,12 +1125,15 @@ hipError_t launch_merge_t(int group, const MergeArgs& args, hipStream_t stream) 
     }
     return hipGetLastError();
   }
+  // 4 waves fold 16 pieces per round trip; more waves only when a segment can have more
+  // pieces (most workgroups of a large batch exit at once, and launching idle waves costs)
   const dim3 grid(args.num_kv_heads, args.batch);
+  auto waves = [&](int most) { return (args.max_pieces <= 16 ? 4 : most) * kWave; };
   switch (group) {
-    case 1: merge_kernel<OT, D, 1><<<grid, merge_waves<1, D>() * kWave, 0, stream>>>(args); break;
-    case 2: merge_kernel<OT, D, 2><<<grid, merge_waves<2, D>() * kWave, 0, stream>>>(args); break;
-    case 4: merge_kernel<OT, D, 4><<<grid, merge_waves<4, D>() * kWave, 0, stream>>>(args); break;
-    case 8: merge_kernel<OT, D, 8><<<grid, merge_waves<8, D>() * kWave, 0, stream>>>(args); break;
+    case 1: merge_kernel<OT, D, 1><<<grid, waves(merge_waves<1, D>()), 0, stream>>>(args); break;
+    case 2: merge_kernel<OT, D, 2><<<grid, waves(merge_waves<2, D>()), 0, stream>>>(args); break;
+    case 4: merge_kernel<OT, D, 4><<<grid, waves(merge_waves<4, D>()), 0, stream>>>(args); break;
+    case 8: merge_kernel<OT, D, 8><<<grid, waves(merge_waves<8, D>()), 0, stream>>>(args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

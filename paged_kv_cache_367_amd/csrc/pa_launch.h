@@ -115,6 +115,7 @@ struct MergeArgs {
   int32_t num_ranges;           // W
   int32_t part_units;
   int32_t chunk_merge;          // default split: 1 = merge_chunk_kernel, 0 = merge_kernel
+  int32_t max_pieces;           // most pieces a segment can be cut into (merge_kernel size)
   float v_scale;
   const float* v_head_scales;   // [Hkv] or null
 };
