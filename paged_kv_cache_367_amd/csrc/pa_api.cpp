@@ -215,14 +215,17 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
   m.group_waves = nw;
   m.num_ranges = W;
   m.part_units = a.part_units;
-  // default split: the per-chunk merge (one round trip for a segment cut once) when a call
-  // can have at least 8 units per chunk; with fewer, a segment may be cut into many pieces
-  // and the per-(kv head, sequence) merge folds 64 of them per round trip
+  // default split: the per-chunk merge (one round trip for a segment cut once; its
+  // workgroup folds longer segments alone, 8 pieces per round trip) when there are at
+  // least W/4 segments and a call can have 8 units per chunk; with fewer segments or
+  // units, segments tend to be cut into many pieces, and the per-(kv head, sequence)
+  // merge spreads them over its workgroups, 64 per round trip
   {
     const int64_t seq_blocks =
         ((int64_t)max_context_len + pa::kBlockTokens - 1) / pa::kBlockTokens;
-    const int64_t max_units = (int64_t)(desc->num_kv_heads / nw) * desc->batch * seq_blocks;
-    m.chunk_merge = max_units >= 8 * (int64_t)W ? 1 : 0;
+    const int64_t segments = (int64_t)(desc->num_kv_heads / nw) * desc->batch;
+    const int64_t max_units = segments * seq_blocks;
+    m.chunk_merge = (4 * segments >= W && max_units >= 8 * (int64_t)W) ? 1 : 0;
     // a segment holds at most seq_blocks units: one piece per partition (plus one when
     // unaligned), or with the default split one per unit at most
     const int pu = part_units(desc);

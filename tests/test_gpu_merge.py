@@ -29,8 +29,9 @@ def _lengths(blocks, seed):
 
 def _run(blocks, num_kv_heads=8, num_q_heads=32, seed=0):
     """Decode the workload twice: with its own table width, and with the tables padded
-    (-1) so wide that a call could have 8 units per chunk, which selects the per-chunk
-    merge; smaller bounds select the per-(kv head, sequence) merge."""
+    (-1) so wide that a call could have 8 units per chunk. With at least W/4 segments the
+    wide run selects the per-chunk merge; fewer segments, or fewer possible units, select
+    the per-(kv head, sequence) merge."""
     import torch
     L = _lengths(blocks, seed)
     w = wl.custom(batch=L.size, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
@@ -63,9 +64,12 @@ def test_segments_of_exactly_one_and_two_chunks():
     _run([8] * 128, seed=1)              # every sequence is exactly two chunks
 
 
-def test_segments_over_many_chunks_with_empty_chunks_and_zero_lengths():
-    # T = 255 < W: one static chunk is empty; the 100-block sequence spans 100 chunks
-    blocks = [100, 0, 50, 60, 0, 30, 10, 5]
+@pytest.mark.parametrize("pad", [0, 56])
+def test_segments_over_many_chunks_with_empty_chunks_and_zero_lengths(pad):
+    # T = 255 < W: one static chunk is empty; the 100-block sequence spans 100 chunks.
+    # With 56 more empty sequences there are W/4 segments, so the wide run takes the
+    # per-chunk merge over the same chunks.
+    blocks = [100, 0, 50, 60, 0, 30, 10, 5] + [0] * pad
     assert sum(blocks) == W - 1
     _run(blocks, seed=2)
 
@@ -87,7 +91,9 @@ def test_two_head_groups_per_sequence():
 
 
 @pytest.mark.parametrize("L", [4096, 8191, 300])
-def test_single_long_sequence(L):
-    # batch 1: the sequence's blocks are spread over every chunk (one unit per chunk for
-    # 4096 tokens), so its merge folds up to 256 pieces
-    _run([-(-L // 16)], seed=5)
+@pytest.mark.parametrize("pad", [0, 63])
+def test_single_long_sequence(L, pad):
+    # one non-empty sequence: its blocks are spread over every chunk (one unit per chunk
+    # for 4096 tokens), so its merge folds up to 256 pieces; with 63 empty sequences
+    # beside it the wide run folds them in the per-chunk merge
+    _run([-(-L // 16)] + [0] * pad, seed=5)
