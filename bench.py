@@ -413,6 +413,10 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None,
                     help="tokens per split-KV partition (default: the workload's, else the library's)")
     ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=None,
+                    help="decode: override the workload's sequence count (its shape otherwise)")
+    ap.add_argument("--context", type=int, nargs=2, default=None, metavar=("MIN", "MAX"),
+                    help="decode: clip the workload's context lengths into [MIN, MAX]")
     ap.add_argument("--path", choices=["decode", "prefill", "swap", "manager"], default="decode",
                     help="decode (the default step), one chunked-prefill step, a block swap "
                          "to pinned host memory and back, or the host block manager")
@@ -462,7 +466,10 @@ def main() -> int:
 
     log(f"building workload {args.config}")
     t0 = time.perf_counter()
-    w = wl.make(args.config)
+    w = wl.make(args.config, batch=args.batch,
+                len_range=tuple(args.context) if args.context else None)
+    if args.batch is not None or args.context is not None:      # not the named workload
+        w.name = f"{w.name}_b{w.batch}_L{int(w.context_lens.min())}-{int(w.context_lens.max())}"
     log(f"workload {w.name}: B={w.batch} tokens={w.total_tokens} kv_bytes={w.kv_bytes} "
         f"pool_blocks={w.num_blocks} ({time.perf_counter() - t0:.1f} s)")
     part = args.partition_size if args.partition_size is not None else w.partition_size
@@ -547,8 +554,7 @@ def main() -> int:
         "tokens_per_s": w.batch / (ms * 1e-3),
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "roofline": {
-            "kernel": "pa_decode (decode_kernel + %s)"
-                      % ("merge_kernel" if part else "merge_chunk_kernel"), "bound": "hbm",
+            "kernel": "pa_decode (decode_kernel + merge kernel)", "bound": "hbm",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
             "launch_ms": dec_avg, "algorithmic_bytes_per_launch": w.kv_bytes,
