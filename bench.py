@@ -34,7 +34,7 @@ the block tables (one pa_bm_tables call); value is steps per second, the oracle'
 manager as baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 3]
-                       [--path decode|prefill|swap|manager]
+                       [--path decode|prefill|swap|manager] [--batch B] [--context MIN MAX]
 """
 from __future__ import annotations
 
