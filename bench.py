@@ -493,7 +493,7 @@ def main() -> int:
     out = torch.empty(tuple(w.q.shape), dtype=out_dtype, device="cuda")
     desc = pa.binding.make_desc(q, ks[0], tables, out, part)
     ws_bytes = pa.pa_decode_workspace_bytes(desc, w.max_context_len)
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     chunks = pa.pa_decode_max_chunks(desc, w.max_context_len)
     torch.cuda.synchronize()
     log(f"resident: {R} pool replicas, workspace {ws_bytes} B, up to {chunks} work chunks")

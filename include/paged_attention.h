@@ -69,11 +69,13 @@ typedef enum {
  *                       every sequence and kv head) is cut into equal contiguous chunks,
  *                       one per workgroup of a fixed grid, whatever the length mix; a
  *                       sequence is cut only where a chunk ends. Otherwise a multiple of
- *                       16 (tokens): every chunk is that long (fixed-size split-KV
- *                       partitions, taken from a counter by whichever workgroup is free),
- *                       so no piece of a sequence is longer. A call whose chunks could
- *                       exceed 16384 is rejected (UNSUPPORTED). The cut points depend on
- *                       the lengths only, so results are bitwise reproducible. */
+ *                       16 (tokens), the split-KV partition: the work is cut into m equal
+ *                       contiguous chunks per workgroup, m the smallest count for which no
+ *                       chunk holds more than partition_size tokens of a sequence and kv
+ *                       head, so no piece of a sequence is longer and every workgroup gets
+ *                       the same work. A call whose chunks could exceed 16384 is rejected
+ *                       (UNSUPPORTED). The cut points depend on the lengths only, so
+ *                       results are bitwise reproducible. */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;
@@ -99,12 +101,12 @@ const char* pa_status_string(int32_t status);
 int32_t pa_decode_max_chunks(const pa_decode_desc_t* desc, int32_t max_context_len);
 
 /* Bytes of device workspace pa_decode needs (0 for an invalid descriptor or B = 0).
- * The workspace holds two chunk counters, for each chunk the (m, l, acc) records of the
- * at most two sequence pieces it leaves unfinished (running max m in log2 units,
- * normaliser l and unnormalised output acc[d], fp32, per kv head and query head), the
- * per-sequence prefix sums of block counts, and per chunk a 16-byte header naming the
- * sequence piece the merge completes there. It must be zero-filled before its first
- * use; every call leaves the counters at zero again, so later calls need no clearing. */
+ * The workspace holds, for each chunk, the (m, l, acc) records of the at most two
+ * sequence pieces it leaves unfinished (running max m in log2 units, normaliser l and
+ * unnormalised output acc[d], fp32, per kv head and query head), the per-sequence prefix
+ * sums of block counts, and per chunk a 16-byte header naming the sequence piece the
+ * merge completes there. Every call writes what it later reads, so the workspace needs
+ * no initialisation. */
 size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_context_len);
 
 /* Decode attention over the paged KV cache.
@@ -126,15 +128,17 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_conte
  *   out            [B, Hq, d] out_dtype, written
  *   q              [B, Hq, d] q_dtype
  *   k_pool, v_pool [N, 16, Hkv, d] kv_dtype (separate K and V pools)
- *   block_tables   [B, maxb] int32; entries past ceil(L/16) are ignored (-1 by convention)
+ *   block_tables   [B, maxb] int32; entries past ceil(L/16) are ignored (-1 by convention).
+ *                  An entry below ceil(L/16) outside [0, N) is a caller error; it is never
+ *                  dereferenced, and its 16 tokens are left out of the softmax (the
+ *                  result is the attention over the sequence's other tokens; zero if none)
  *   context_lens   [B] int32, each in [0, min(maxb*16, max_context_len)]
  *   max_context_len host int >= every context_lens[b]; sizes the launch (no device sync)
  *   scale          host float, usually 1/sqrt(d)
  *   k_scale, v_scale host floats, dequantisation scales for fp8 pools (use 1 otherwise)
  *   workspace, workspace_bytes  device scratch of at least pa_decode_workspace_bytes()
- *                  (always needed when B > 0), zero-filled before its first use (see
- *                  pa_decode_workspace_bytes); calls that share a workspace must not
- *                  overlap
+ *                  (always needed when B > 0), any contents; calls that share a
+ *                  workspace must not overlap
  * All pointers must be 16-byte aligned. */
 pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
                       const void* k_pool, const void* v_pool,
@@ -186,7 +190,9 @@ typedef struct {
  *                  rows of each sequence
  *   q              [Tq, Hq, d] q_dtype
  *   k_pool, v_pool [N, 16, Hkv, d] kv_dtype
- *   block_tables   [B, maxb] int32; entries past ceil(L/16) are ignored
+ *   block_tables   [B, maxb] int32; entries past ceil(L/16) are ignored; an entry below it
+ *                  outside [0, N) is never read and its 16 positions are left out of
+ *                  every row's softmax (a caller error, as for pa_decode)
  *   context_lens   [B] int32, each in [0, maxb*16] (larger values are clamped)
  *   query_start    [B + 1] int32, non-decreasing from 0 to Tq
  *   max_query_len  host int >= every n; sizes the launch (no device sync); at most

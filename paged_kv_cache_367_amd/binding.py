@@ -138,11 +138,11 @@ def pa_decode_max_chunks(desc: DecodeDesc, max_context_len: int) -> int:
 
 
 def decode_workspace(desc: DecodeDesc, max_context_len: int, device="cuda"):
-    """A zero-filled workspace tensor for pa_decode (zero before first use; pa_decode
-    leaves it ready for the next call)."""
+    """A workspace tensor for pa_decode (its contents need no initialisation: every call
+    writes what it reads)."""
     import torch
     n = load_library().pa_decode_workspace_bytes(ctypes.byref(desc), int(max_context_len))
-    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def pa_decode_workspace_bytes(desc: DecodeDesc, max_context_len: int) -> int:
@@ -166,9 +166,8 @@ def _head_scale_ptrs(k_scale, v_scale, num_kv_heads):
 def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
               scale: float, k_scale=1.0, v_scale=1.0, workspace=None,
               partition_size: int = 0, stream=None):
-    """Decode attention into `out` [B, Hq, d]. workspace: a zero-initialised uint8 GPU
-    tensor of at least pa_decode_workspace_bytes() bytes (allocated here, zero-filled,
-    when None). k_scale / v_scale: floats, or float32 [Hkv] GPU tensors of per-head scales
+    """Decode attention into `out` [B, Hq, d]. workspace: a uint8 GPU tensor of at least
+    pa_decode_workspace_bytes() bytes, any contents (allocated here when None). k_scale / v_scale: floats, or float32 [Hkv] GPU tensors of per-head scales
     (pa_decode_head_scales)."""
     import torch
     lib = load_library()
@@ -181,7 +180,7 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_le
     desc = make_desc(q, k_pool, block_tables, out, partition_size)
     need = lib.pa_decode_workspace_bytes(ctypes.byref(desc), int(max_context_len))
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     per_head, ks, vs, kp, vp = _head_scale_ptrs(k_scale, v_scale, k_pool.shape[2])

@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <limits.h>
 
+#include <atomic>
+
 #include "../../include/paged_attention.h"
 #include "pa_launch.h"
 
@@ -34,9 +36,33 @@ bool supported_combo(int32_t q, int32_t kv, int32_t out) {
   return false;
 }
 
-// Workgroups of the decode: 8 waves per CU on the 256 CUs, NW waves each.
+// Most workgroups a decode grid has: 8 waves per CU on at most kMaxDeviceCUs CUs, NW
+// waves each. The workspace is sized for this many static chunks.
+int max_workgroups(const pa_decode_desc_t* d) {
+  return pa::kMaxDeviceCUs * pa::kWavesPerCU / pa::group_waves(d->num_kv_heads);
+}
+
+// Compute units of the current device (queried once per device), capped at kMaxDeviceCUs;
+// kMaxDeviceCUs when the query fails.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return pa::kMaxDeviceCUs;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = pa::kMaxDeviceCUs;
+    n = n < pa::kMaxDeviceCUs ? n : pa::kMaxDeviceCUs;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroups of this call's decode grid: 8 waves per CU of the current device.
 int num_workgroups(const pa_decode_desc_t* d) {
-  return pa::kDeviceCUs * pa::kWavesPerCU / pa::group_waves(d->num_kv_heads);
+  return device_cus() * pa::kWavesPerCU / pa::group_waves(d->num_kv_heads);
 }
 
 // Units per chunk for an explicit partition size (0: default split).
@@ -45,7 +71,7 @@ int part_units(const pa_decode_desc_t* d) { return d->partition_size / pa::kBloc
 // Most chunks a call can have, which sizes the records in the workspace: the W static
 // ones, plus with fixed partitions every partition of the largest possible unit count.
 int64_t max_chunks(const pa_decode_desc_t* d, int32_t max_context_len) {
-  const int W = num_workgroups(d);
+  const int W = max_workgroups(d);
   const int pu = part_units(d);
   if (pu == 0) return W;
   const int nw = pa::group_waves(d->num_kv_heads);
@@ -90,10 +116,10 @@ pa_status_t check_desc(const pa_decode_desc_t* d, int32_t max_context_len) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: the two chunk counters (zero between calls), the records of cut segments,
-// the per-sequence block prefix sums, then one 16-byte header per chunk.
+// Workspace: the records of cut segments, the per-sequence block prefix sums, then one
+// 16-byte header per chunk. Every call writes what it reads, so no clearing is needed.
 struct Workspace {
-  size_t counters, acc, ml, prefix, hdr, total;   // byte offsets and size
+  size_t acc, ml, prefix, hdr, total;   // byte offsets and size
 };
 Workspace workspace_layout(const pa_decode_desc_t* d, int32_t max_context_len) {
   const size_t chunks = (size_t)max_chunks(d, max_context_len);
@@ -101,8 +127,7 @@ Workspace workspace_layout(const pa_decode_desc_t* d, int32_t max_context_len) {
   const size_t group = (size_t)(d->num_q_heads / d->num_kv_heads);
   const size_t recs = chunks * 2 * nw * group;       // (chunk, slot, wave, q head)
   Workspace w;
-  w.counters = 0;
-  w.acc = 256;
+  w.acc = 0;
   w.ml = w.acc + align_up(recs * d->head_dim * sizeof(float), 256);
   w.prefix = w.ml + align_up(recs * 2 * sizeof(float), 256);
   w.hdr = w.prefix + align_up(((size_t)d->batch + 1) * sizeof(int32_t), 256);
@@ -179,7 +204,6 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.counters = reinterpret_cast<int32_t*>(wsb + ws.counters);
   a.rec_acc = reinterpret_cast<float*>(wsb + ws.acc);
   a.rec_ml = reinterpret_cast<float*>(wsb + ws.ml);
   a.prefix = reinterpret_cast<int32_t*>(wsb + ws.prefix);
@@ -226,11 +250,9 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
     const int64_t segments = (int64_t)(desc->num_kv_heads / nw) * desc->batch;
     const int64_t max_units = segments * seq_blocks;
     m.chunk_merge = (4 * segments >= W && max_units >= 8 * (int64_t)W) ? 1 : 0;
-    // a segment holds at most seq_blocks units: one piece per partition (plus one when
-    // unaligned), or with the default split one per unit at most
-    const int pu = part_units(desc);
-    const int64_t pieces = pu > 0 ? (seq_blocks + pu - 1) / pu + 1 : seq_blocks;
-    m.max_pieces = (int32_t)(pieces < INT32_MAX ? pieces : INT32_MAX);
+    // a segment holds at most seq_blocks units, so at most that many pieces (chunks can
+    // be shorter than a partition when the batch has few units)
+    m.max_pieces = (int32_t)(seq_blocks < INT32_MAX ? seq_blocks : INT32_MAX);
   }
   m.v_scale = v_scale;
   m.v_head_scales = v_heads;

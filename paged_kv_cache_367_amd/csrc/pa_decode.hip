@@ -11,7 +11,7 @@
 // How it maps onto CDNA4
 //   * Persistent, balanced work split. A unit is one 16-token block of one sequence for
 //     one head group of NW kv heads (NW = 8 when Hkv allows). Units are numbered
-//     sequence by sequence; a fixed grid of W workgroups (8 waves per CU on the 256 CUs)
+//     sequence by sequence; a fixed grid of W workgroups (8 waves per CU of the device)
 //     takes equal contiguous shares, whatever the length mix. Wave w of a workgroup
 //     handles kv head hg*NW + w, so the NW waves read the NW head slices of the same
 //     blocks at the same time: each token row is read as one contiguous stretch.
@@ -20,25 +20,33 @@
 //     of the NBUF after those are in flight. K/V loads are raw buffer loads from a
 //     per-block scalar descriptor; a unit past the share gets an empty descriptor, so
 //     the instruction stream (and every wait count) is the same at every step.
-//   * QK^T runs on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}, fp8 converted to
-//     bf16 first, v_mfma_f32_16x16x4f32 for fp32). Operand B is the K block exactly as
-//     it sits in HBM: lane (t, q) = (lane % 16, lane / 16) loads 16-byte chunk 4s+q of
-//     token t's row. Operand A repeats the G query rows over the 16 MFMA rows (row i
-//     holds head i % G), so after the MFMA every lane holds its token's scores for the
-//     G heads. The q rows arrive with the first block of a piece and are laid out for
-//     the MFMA through LDS.
-//   * Block max: 16-lane DPP row reduction. Probabilities p[t][h] go to LDS once per
-//     block and are read back broadcast by the V stage.
-//   * PV on the vector ALU in fp32: lane (r, c) owns a V chunk c of rows r, r + RPI, ...
-//     and accumulates acc[h][e] for all G heads, so every V byte is converted once and
-//     used G times. At the end of a piece, lanes owning the same chunk are summed.
+//   * 16-bit and fp8 K/V: scores are computed as K.Q^T on the matrix cores
+//     (v_mfma_f32_16x16x32_{bf16,f16}; fp8 is widened exactly to bf16 first). Operand A
+//     is the K block exactly as it sits in HBM: lane (t, q) = (lane % 16, lane / 16) loads
+//     16-byte chunk 4s+q of token t's row. Operand B repeats the G query rows over the 16
+//     MFMA columns (column n holds head n % G), laid out once per piece through LDS. The
+//     MFMA's output leaves lane (n, kq) with the scores of tokens 4kq .. 4kq+3 for head
+//     n % G, which is the A-operand layout of P in P.V, so P never leaves registers.
+//   * Block max: in-lane over the 4 tokens, then v_permlane16/32_swap across the 4 row
+//     groups; the running (m, l) and the rescale of the accumulators stay in registers.
+//   * P.V on the matrix cores (v_mfma_f32_16x16x32 in the K/V element type): the 32-deep
+//     contraction takes the 16-bit hi part and the 16-bit lo part of every weight p against
+//     the same V row, so the weights enter within 2^-16 of their fp32 value; l sums the
+//     fp32 weights. Lane (n, kq) loads dims D/16*n .. of tokens 4kq .. 4kq+3; the B operand
+//     is two byte permutes away.
+//   * fp32 K/V: QK^T on v_mfma_f32_16x16x4f32, p through LDS, and P.V on the vector ALU in
+//     fp32: lane (r, c) owns V chunk c of rows r, r + RPI, ... for all G heads; lanes
+//     owning the same chunk are summed at the end of a piece.
 //   * A sequence whose segment lies in one share is written out directly. A segment cut
 //     by share boundaries leaves one (m, l, acc) record per piece (at most two per wave:
 //     the share's first and last segment), and a merge kernel combines them
 //     (merge_chunk_kernel: one workgroup per chunk, named by a header the decode
-//     writes; with fixed partitions merge_kernel, one per (kv head, sequence)).
-//   * The partial last block is masked by selection (scores -> -inf, V -> 0), so stale
-//     or NaN slots past L never reach the result.
+//     writes; with fixed partitions merge_kernel, one per (kv head, sequence)). With
+//     fixed partitions a workgroup takes a contiguous run of partitions, assigned
+//     statically from the lengths.
+//   * The partial last block is masked by selection (scores -> -inf, V rows read as 0), so
+//     stale or NaN slots past L never reach the result. A block id outside the pool is
+//     never dereferenced; its 16 tokens are masked the same way.
 //   * Reduction order depends on logical positions and lengths only, never on physical
 //     block ids, so moving blocks in the pool leaves the output bitwise unchanged.
 
@@ -123,16 +131,6 @@ __device__ __forceinline__ void v_words16(const VTy& w, uint32_t (&o)[WORDS]) {
     for (int i = 0; i < WORDS; ++i) o[i] = w[i];
   }
 }
-// One 16x16x16 MFMA in the element type of KV (fp16 for fp16, bf16 otherwise).
-template <int KV>
-__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
-  if constexpr (KV == PA_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
 // Matrix-core path: scores as K.Q^T, so that the MFMA's output layout (lane (n, kq): rows
 // 4kq + v, column n) gives each lane tokens 4kq .. 4kq+3 of head n % G, which is the A
 // operand layout P takes in P.V. One 16-byte K chunk (A) against the matching q piece(s)
@@ -163,30 +161,57 @@ __device__ __forceinline__ f32x4 kq_chunk(f32x4 acc, u32x4 k, const u32x4* qc) {
   }
   return acc;
 }
-// p of four tokens rounded to the P.V element type (fp16 for fp16 K/V, else bf16, round to
-// nearest even) and packed as the MFMA A operand; pr gets the rounded values as fp32.
+// p of four tokens as the A operand of a 16x16x32 P.V MFMA: elements 0..3 hold hi(p) of
+// tokens 4kq .. 4kq+3 and elements 4..7 lo(p), the remainder p - hi(p) in the same 16-bit
+// type; the B operand repeats the four V rows, so the product takes sum (hi + lo) v. bf16:
+// hi is p with its low 16 bits cleared (exact, relative error below 2^-7), lo that
+// remainder rounded to nearest even, so hi + lo is p to within 2^-16 relative. fp16: hi
+// and lo rounded to nearest even (within 2^-22).
 template <int KV>
-__device__ __forceinline__ u32x2 round_pack4(const float (&p)[4], float (&pr)[4]) {
+__device__ __forceinline__ u32x4 split_pack4(const float (&p)[4]) {
+  u32x4 a;
   if constexpr (KV == PA_F16) {
-    _Float16 h[4];
+    _Float16 h[4], l[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       h[v] = (_Float16)p[v];
-      pr[v] = (float)h[v];
+      l[v] = (_Float16)(p[v] - (float)h[v]);
     }
-    return u32x2{(uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
-                     (uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16,
-                 (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
-                     (uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16};
+    auto pk = [](_Float16 x, _Float16 y) {
+      return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+             (uint32_t)__builtin_bit_cast(uint16_t, y) << 16;
+    };
+    a[0] = pk(h[0], h[1]);
+    a[1] = pk(h[2], h[3]);
+    a[2] = pk(l[0], l[1]);
+    a[3] = pk(l[2], l[3]);
   } else {
-    const bf16x2 lo = {(__bf16)p[0], (__bf16)p[1]}, hi = {(__bf16)p[2], (__bf16)p[3]};
-    const u32x2 a = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-    pr[0] = __uint_as_float(a[0] << 16);
-    pr[1] = __uint_as_float(a[0] & 0xffff0000u);
-    pr[2] = __uint_as_float(a[1] << 16);
-    pr[3] = __uint_as_float(a[1] & 0xffff0000u);
-    return a;
+    uint32_t b[4];
+    float r[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      b[v] = __float_as_uint(p[v]);
+      r[v] = p[v] - __uint_as_float(b[v] & 0xffff0000u);   // exact
+    }
+    a[0] = __builtin_amdgcn_perm(b[1], b[0], 0x07060302u);   // upper halves of p0, p1
+    a[1] = __builtin_amdgcn_perm(b[3], b[2], 0x07060302u);
+    const bf16x2 l01 = {(__bf16)r[0], (__bf16)r[1]}, l23 = {(__bf16)r[2], (__bf16)r[3]};
+    a[2] = __builtin_bit_cast(uint32_t, l01);
+    a[3] = __builtin_bit_cast(uint32_t, l23);
   }
+  return a;
+}
+// P.V on a 16x16x32 MFMA in the element type of KV (fp16 for fp16, bf16 otherwise): the
+// A operand from split_pack4, the B operand the lane's four V values (two words) twice.
+template <int KV>
+__device__ __forceinline__ f32x4 mfma_pv(u32x4 a, u32x2 b, f32x4 c) {
+  const u32x4 bb = {b[0], b[1], b[0], b[1]};
+  if constexpr (KV == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, bb), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, bb), c, 0, 0, 0);
 }
 // DPP quad broadcast: every lane gets the value of lane I of its quad
 template <int I>
@@ -285,7 +310,6 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ int s_lens[kMaxBatch];        // clamped context length per sequence
   __shared__ int s_pre[kMaxBatch + 1];     // blocks before each sequence
   __shared__ int s_wsum[kMaxGroupWaves];
-  __shared__ int s_next[2];                // next chunk of the workgroup, by parity
   __shared__ float s_p[kMaxGroupWaves][2 * PBUF];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[kMaxGroupWaves][QBYTES];
 
@@ -336,18 +360,15 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- 2. chunks. T units. By default workgroup r takes static chunk r, dealt to the 8
-  // XCDs in contiguous eighths (workgroups go to XCDs round-robin) so that neighbouring
-  // sequences share an L2. With fixed partitions every chunk is taken from a counter.
-  const int W = a.num_ranges, bid = blockIdx.x;
-  const ChunkGeom cg = chunk_geometry((int64_t)HGC * total, W, a.part_units);
-  const int rng = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
-  int* const grab_ctr = a.counters;          // small chunks taken
-  int* const done_ctr = a.counters + 1;      // workgroups that found none left
-  uint32_t grab_v = 0;                       // wave 0, lane 0: pending counter value
-  uint32_t done_v = 0;
-  bool done_issued = false;
-  int tpar = 0;                              // parity of the chunk transition
+  // ---- 2. chunks. T units in W equal static chunks, m per workgroup (m = 1 by default;
+  // with fixed partitions just enough that no chunk exceeds the partition). Workgroup r
+  // takes chunks r*m .. r*m + m - 1, the r dealt to the 8 XCDs in contiguous eighths
+  // (workgroups go to XCDs round-robin) so that neighbouring sequences share an L2.
+  const int W0 = a.num_ranges, bid = blockIdx.x;
+  const ChunkGeom cg = chunk_geometry((int64_t)HGC * total, W0, a.part_units);
+  const int W = cg.W;
+  const int rng = (W0 % 8 == 0) ? (bid % 8) * (W0 / 8) + bid / 8 : bid;
+  const int c_last = rng * cg.per_wg + cg.per_wg - 1;
   __syncthreads();
 
   // ---- 3. the unit walker (scalar): position in the current chunk, sequence, head
@@ -374,12 +395,6 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     whg = uni(rel / wnb);   // integer division runs on the vector ALU
     wj = rel - whg * wnb;
   };
-  // Ask for the chunk after the current one. atomicInc (increment with a wrap bound that
-  // is never reached) rather than atomicAdd: the compiler turns a uniform atomicAdd into a
-  // wave-wide atomic whose result it waits for at once, which would drain the load ring.
-  auto grab = [&]() {
-    if (wave == 0 && lane == 0) grab_v = atomicInc(reinterpret_cast<unsigned*>(grab_ctr), ~0u);
-  };
   // Header of the static chunk for merge_chunk_kernel (default split only): the segment
   // whose last piece opens the chunk, if it began in an earlier chunk. Noted at entry,
   // written once the first loads are in flight (its divisions are then off the path to
@@ -398,34 +413,22 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     cend = uni((int)chunk_end(cg, c));
     wu = cbeg;
     locate(wu);
-    grab();
-    if (!cg.fixed && c < W) {
+    if (!cg.fixed) {
       const int sseg = HGC * uni(s_pre[wb]) + whg * wnb;
       note_header(c, wj > 0 && sseg + wnb <= cend, sseg);
     }
   };
-  // at a chunk end: wave 0 publishes the chunk it was given, all waves take it
-  auto next_chunk = [&]() {
-    if (wave == 0 && lane == 0) {
-      const bool none = grab_v >= (uint32_t)cg.nsmall;
-      s_next[tpar] = none ? -1 : W + (int)grab_v;
-      if (none && !done_issued) {
-        done_v = atomicInc(reinterpret_cast<unsigned*>(done_ctr), ~0u);
-        done_issued = true;
-      }
-    }
-    __syncthreads();
-    const int c = __builtin_amdgcn_readfirstlane(s_next[tpar]);
-    tpar ^= 1;
-    enter(c);
+  // the workgroup's first non-empty chunk after c, or -1
+  auto next_nonempty = [&](int c) {
+    for (++c; c <= c_last; ++c)
+      if (chunk_begin(cg, c) < chunk_end(cg, c)) return c;
+    return -1;
   };
-  if (!cg.fixed && chunk_begin(cg, rng) < chunk_end(cg, rng)) {
-    enter(rng);
-  } else {
-    if (!cg.fixed) note_header(rng, false, 0);   // an empty static chunk ends no segment
-    grab();
-    next_chunk();
-  }
+  // at a chunk end: the workgroup's next chunk, or none
+  auto next_chunk = [&]() { enter(next_nonempty(cur)); };
+  if (!cg.fixed && chunk_begin(cg, rng) == chunk_end(cg, rng))
+    note_header(rng, false, 0);   // an empty chunk ends no segment
+  enter(next_nonempty(rng * cg.per_wg - 1));
   // default split: sequences of length 0 own no units; workgroup r writes the zero
   // outputs of sequences r, r + W, ... (with fixed partitions the merge does)
   if (!cg.fixed) {
@@ -488,10 +491,13 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   };
   // K, V of the unit's block for this wave's kv head, and the head's q rows when the
   // unit opens a piece. Always the same instructions, so wait counts stay static.
-  auto issue = [&](const UnitMeta& m, uint32_t idv, u32x4(&kb)[NL], VT(&vb)[NLV],
+  // A block id outside [0, num_blocks) is never dereferenced: its unit keeps rem = 0, so
+  // all 16 of its tokens are masked out of the softmax like rows past L.
+  auto issue = [&](UnitMeta& m, uint32_t idv, u32x4(&kb)[NL], VT(&vb)[NLV],
                    u32x4(&qs)[QPL]) {
     const int pid = __builtin_amdgcn_readfirstlane((int)idv);
     const bool valid = (m.flags() & kValid) && (unsigned)pid < (unsigned)a.num_blocks;
+    if (!valid) m.bf &= 0x00ffffff;
     const int g = m.hg() * NW + wave;
     const size_t base = valid ? (size_t)pid * blk_stride + (size_t)g * ROWB : 0;
     // rows at or past L (the block's last rem tokens are valid) read as zero, unfetched
@@ -582,13 +588,14 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       const float bm = b01 > b23 ? b01 : b23;
       const float mn = xrow_max(bm > m1 ? bm : m1);
       const float al1 = mn == neg_inf() ? 1.0f : fast_exp2(m1 - mn);
-      float pf[4], pr[4];
+      // (mn is -inf only while every token so far was masked: then every p is 0)
+      const float mref = mn == neg_inf() ? 0.0f : mn;
+      float pf[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) pf[v] = fast_exp2(sv[v] - mn);   // 0 for masked tokens
-      // the matrix cores take p in 16 bits; l sums the same rounded weights, so the output
-      // stays an exact weighted average of the V rows
-      const u32x2 aop = round_pack4<KV>(pf, pr);
-      l1 = l1 * al1 + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      for (int v = 0; v < 4; ++v) pf[v] = fast_exp2(sv[v] - mref);   // 0 for masked tokens
+      // the matrix cores take p in 16 bits, as a hi and a lo part (within 2^-16 of p)
+      const u32x4 aop = split_pack4<KV>(pf);
+      l1 = l1 * al1 + ((pf[0] + pf[1]) + (pf[2] + pf[3]));
       m1 = mn;
       // rescale: accumulator row 4kq + v belongs to head (4kq + v) % G, whose factor lives
       // in the lanes of column n with n % G == that head
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const u32x2 bop = {__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
                            __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel)};
-        acc4[e] = mfma16<KV>(aop, bop, acc4[e]);
+        acc4[e] = mfma_pv<KV>(aop, bop, acc4[e]);
       }
     } else {
       // vector-ALU P.V (fp32 K/V). Scores of token t = lane % 16 for the heads of MFMA rows
@@ -826,11 +833,6 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     for (int u = 0; u < R; ++u) busy |= ((mk[u].flags() | mi[u].flags()) & kValid) != 0;
     if (!busy) break;
   }
-  // the last workgroup to run out of chunks resets the counters for the next call
-  if (wave == 0 && lane == 0 && done_issued && done_v == (uint32_t)(W - 1)) {
-    atomicExch(grab_ctr, 0);
-    atomicExch(done_ctr, 0);
-  }
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -906,18 +908,13 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
   const int64_t S = (int64_t)HGC * c0 + (int64_t)hg * nb, E = S + nb - 1;
   const ChunkGeom cg = chunk_geometry(T, a.num_ranges, a.part_units);
   const int W = cg.W;
-  // The segment's pieces, in unit order: with fixed partitions small chunks W + u / P
-  // (u < 2^31, P < 2^16), all non-empty; with the default split, static chunks, which
-  // hold at most one unit each when T < W (then a piece per unit, in chunk
-  // ((u + 1) W - 1) / T, so the empty chunks between them are never visited).
-  const bool by_unit = !cg.fixed && T < W;
+  // The segment's pieces, in unit order: the chunks it overlaps, which hold at most one
+  // unit each when T < W (then a piece per unit, in chunk ((u + 1) W - 1) / T, so the
+  // empty chunks between them are never visited; 32-bit: u < T < W <= kMaxChunks).
+  const bool by_unit = T < W;
   const int Ti = (int)T, Si = (int)S, Ei = (int)E;
   int cf, np;
-  if (cg.fixed) {
-    const int P = (int)cg.C2;
-    cf = W + Si / P;
-    np = W + Ei / P - cf + 1;
-  } else if (by_unit) {
+  if (by_unit) {
     cf = ((Si + 1) * W - 1) / Ti;
     np = Ei - Si + 1;
   } else {

@@ -10,7 +10,7 @@ namespace pa {
 
 constexpr int kBlockTokens = 16;      // tokens per KV block (the only supported size)
 constexpr int kMaxGroupWaves = 8;     // waves per decode workgroup (= kv heads per head group)
-constexpr int kDeviceCUs = 256;       // compute units of an MI355X (gfx950)
+constexpr int kMaxDeviceCUs = 256;    // the grid uses at most this many CUs (an MI355X has 256)
 constexpr int kWavesPerCU = 8;        // decode registers are sized for 2 waves per SIMD
 constexpr int kMaxPartitionTokens = 1 << 20;
 constexpr int kMaxBatch = 4096;       // lengths and prefix sums of the batch sit in LDS
@@ -23,27 +23,29 @@ constexpr int kMaxBatch = 4096;       // lengths and prefix sums of the batch si
 // A segment cut by a chunk boundary leaves one (m, l, acc) record per piece, which
 // merge kernels combine; a segment inside one chunk is written out directly.
 //
-// Chunks of [0, T), numbered in unit order. Default: W static chunks, chunk r =
-// [T*r/W, T*(r+1)/W), one per workgroup (a chunk may be empty when T < W). With a fixed
-// partition of P blocks: nsmall chunks of P units (the last may be shorter), numbered
-// from W and taken from a counter by whichever workgroup is free.
+// Chunks of [0, T), numbered in unit order: W equal static chunks, chunk c =
+// [T*c/W, T*(c+1)/W) (a chunk may be empty when T < W), workgroup r of the W0 in the grid
+// taking the contiguous run r*m .. r*m + m - 1. Default split: m = 1 (W = W0). With a
+// fixed partition of P units: m = ceil(T / (W0 P)), the smallest number of chunks per
+// workgroup for which no chunk holds more than P units.
 struct ChunkGeom {
-  int64_t T, C2;
-  int W, nsmall;
+  int64_t T;
+  int W, per_wg;      // chunks, chunks per workgroup (m)
   bool fixed;
   int q, r, wshift;   // T = q * W + r; wshift = log2(W) when W is a power of two, else -1
 };
 constexpr int64_t kMaxChunks = 16384;
 
-// T < 2^31 (the host checks unit counts) and W <= 2048, so static chunk bounds need only
-// 32-bit products, and a shift when W is a power of two (it is for every head count).
-__host__ __device__ inline ChunkGeom chunk_geometry(int64_t T, int W, int fixed_units) {
+// T < 2^31 (the host checks unit counts) and W <= kMaxChunks, so static chunk bounds need
+// only 32-bit products (r * c < W^2 < 2^28), and a shift when W is a power of two.
+__host__ __device__ inline ChunkGeom chunk_geometry(int64_t T, int W0, int fixed_units) {
   ChunkGeom g;
   g.T = T;
-  g.W = W;
   g.fixed = fixed_units > 0;
-  g.C2 = g.fixed ? fixed_units : 1;
-  g.nsmall = g.fixed ? (int)((T + fixed_units - 1) / fixed_units) : 0;
+  const int64_t per = (int64_t)W0 * (fixed_units > 0 ? fixed_units : 1);
+  g.per_wg = g.fixed && T > per ? (int)((T + per - 1) / per) : 1;
+  g.W = W0 * g.per_wg;
+  const int W = g.W;
   g.wshift = (W & (W - 1)) == 0 ? __builtin_ctz((unsigned)W) : -1;
   const int Ti = (int)T;
   g.q = g.wshift >= 0 ? Ti >> g.wshift : Ti / W;
@@ -56,18 +58,13 @@ __host__ __device__ inline int64_t static_bound(const ChunkGeom& g, int c) {
   return (int64_t)g.q * c + (g.wshift >= 0 ? rc >> g.wshift : rc / g.W);
 }
 __host__ __device__ inline int64_t chunk_begin(const ChunkGeom& g, int c) {
-  if (c < g.W) return g.fixed ? 0 : static_bound(g, c);
-  return (int64_t)(c - g.W) * g.C2;
+  return static_bound(g, c);
 }
 __host__ __device__ inline int64_t chunk_end(const ChunkGeom& g, int c) {
-  if (c < g.W) return g.fixed ? 0 : static_bound(g, c + 1);
-  const int64_t e = chunk_begin(g, c) + g.C2;
-  return e > g.T ? g.T : e;
+  return static_bound(g, c + 1);
 }
-// chunk holding unit u (0 <= u < T): the last static chunk starting at or before u, or
-// the taken chunk u / P
+// chunk holding unit u (0 <= u < T): the last chunk starting at or before u
 __host__ __device__ inline int chunk_of(const ChunkGeom& g, int64_t u) {
-  if (g.fixed) return g.W + (int)(u / g.C2);
   return (int)(((u + 1) * g.W - 1) / g.T);
 }
 
@@ -78,7 +75,6 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_tables;  // [B, maxb]
   const int32_t* context_lens;  // [B]
-  int32_t* counters;            // [2] small chunks taken, workgroups done (zero between calls)
   float* rec_acc;               // [chunks, 2, NW, G, d]  unnormalised partial outputs
   float* rec_ml;                // [chunks, 2, NW, G, 2]  (running max m in log2 units, sum l)
   int32_t* prefix;              // [B + 1] blocks before each sequence (workgroup 0 writes)
@@ -91,8 +87,8 @@ struct DecodeArgs {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t num_ranges;           // W, workgroups
-  int32_t part_units;           // fixed chunk length in units, 0 = default split
+  int32_t num_ranges;           // W0, workgroups
+  int32_t part_units;           // most units a chunk may hold, 0 = default split
   float qk_scale_log2;          // scale * k_scale * log2(e), per-tensor scales
   float v_scale;
   const float* k_head_scales;   // [Hkv] per-head dequantisation scales, or null (per tensor):
@@ -112,7 +108,7 @@ struct MergeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group_waves;          // NW
-  int32_t num_ranges;           // W
+  int32_t num_ranges;           // W0, decode workgroups
   int32_t part_units;
   int32_t chunk_merge;          // default split: 1 = merge_chunk_kernel, 0 = merge_kernel
   int32_t max_pieces;           // most pieces a segment can be cut into (merge_kernel size)

@@ -30,7 +30,8 @@
 //     work; l sums p itself). fp8 K/V, whose own rounding is far coarser, takes the
 //     single bf16 pass.
 //   * Tiles wholly at or before the tile's first query position need no mask; the rest
-//     mask positions past each row's own.
+//     mask positions past each row's own. A block id outside the pool is never read; its
+//     16 tokens get a score of -inf (weight 0) in every row.
 //   * Workgroup ids are dealt so that all query tiles of one (sequence, kv head) land on
 //     the same XCD (workgroups go to the 8 XCDs round-robin) and share its L2; within a
 //     pair, later tiles (longer key ranges) start first.
@@ -169,7 +170,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   // fma, which needs a scale >= 0: a negative one is moved onto q (an exact sign flip).
   const float qks_signed =
       a.k_head_scales ? (a.qk_scale * a.k_head_scales[kvh]) * kLog2e : a.qk_scale_log2;
-  const float qks = fabsf(qks_signed);
+  // (at least the smallest normal float, so that a masked score of -inf times it stays
+  // -inf; finite scores times it round to equal weights, as with a zero scale)
+  const float qks = fmaxf(fabsf(qks_signed), __FLT_MIN__);
   const uint32_t qflip = qks_signed < 0.0f ? 0x80008000u : 0u;
   const float vsc = a.v_head_scales ? a.v_head_scales[kvh] : a.v_scale;
 
@@ -213,6 +216,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       make_rsrc(a.block_tables + (size_t)b * a.max_blocks_per_seq, (uint32_t)nb * 4u);
   auto load_ids = [&](int kt) -> u32x4 { return buf_load16(rt, (uint32_t)kt * 16u); };
   const bool stager = kPrefillThreads == kStageThreads || wave < kStageThreads / kWave;
+  // blocks of tile kt below L whose id lies outside the pool (bit i: block 4kt + i): they
+  // are never read, and their 16 tokens are masked out of the softmax
+  auto bad_blocks = [&](int kt, const u32x4& idv) -> int {
+    int bad = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rem = L - (kt * 4 + i) * kBlockTokens;
+      bad |= (rem > 0 && (uint32_t)uni((int)idv[i]) >= (uint32_t)a.num_blocks) ? 1 << i : 0;
+    }
+    return uni(bad);
+  };
   auto stage = [&](int kt, const u32x4& idv, LT (&kr)[4], LT (&vr)[4]) {
     if (!stager) return;
 #pragma unroll
@@ -276,7 +290,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     for (int e = 0; e < DPL; ++e) acc[rg][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  auto compute = [&](int buf, int kt, auto masked_tag) {
+  auto compute = [&](int buf, int kt, int bad, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* Kt = s_k[buf];
     const uint8_t* Vt = s_v[buf];
@@ -294,6 +308,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int c = 0; c < NC; ++c) z = mfma32<CT>(kop[c], qop[rg][c], z);
         sc[rg][s] = z;
+        if (bad & (1 << s)) sc[rg][s] = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
       }
     }
     u32x4 aop[RG][2];                      // P as the A operand, two subtiles per MFMA
@@ -391,8 +406,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   // ---- the key loop: stage tile kt + 1 (ids one tile further ahead) while computing kt
   u32x4 idv = {0u, 0u, 0u, 0u};
   LT kr[4], vr[4];
+  int bad_next = 0;                        // bad blocks of the tile staged last
   if (ntiles > 0) {
     idv = load_ids(0);
+    bad_next = bad_blocks(0, idv);
     stage(0, idv, kr, vr);
     idv = load_ids(1);
     to_lds(0, kr, vr);
@@ -400,11 +417,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   __syncthreads();
   auto step = [&](int kt, auto masked_tag) {
     const bool more = kt + 1 < ntiles;
+    const int bad = bad_next;
     if (more) {
+      bad_next = bad_blocks(kt + 1, idv);
       stage(kt + 1, idv, kr, vr);
       idv = load_ids(kt + 2);
     }
-    compute(kt & 1, kt, masked_tag);
+    compute(kt & 1, kt, bad, masked_tag);
     if (more) to_lds((kt + 1) & 1, kr, vr);
     __syncthreads();
   };

@@ -99,12 +99,3 @@ def max_abs_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     assert gpu.shape == ref.shape
     assert np.isfinite(gpu).all(), "non-finite GPU output"
     return float(np.max(np.abs(gpu - ref))) if gpu.size else 0.0
-
-
-def sample_seqs(w, n=8, seed=0):
-    """Shortest, longest and a seeded random handful of sequences."""
-    L = w.context_lens
-    rng = np.random.default_rng(seed)
-    picks = {int(np.argmin(L)), int(np.argmax(L))}
-    picks |= set(int(x) for x in rng.choice(w.batch, size=min(n, w.batch), replace=False))
-    return sorted(picks)

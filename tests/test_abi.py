@@ -59,7 +59,7 @@ def _decode(lib, desc, max_ctx=8192, ptr=0x10000, ws=None, ws_bytes=0, scale=0.0
 def _ws_bytes(chunks, nw, G, d, B):
     up = lambda x: (x + 255) // 256 * 256
     recs = chunks * 2 * nw * G
-    return 256 + up(recs * d * 4) + up(recs * 2 * 4) + up((B + 1) * 4) + up(chunks * 16)
+    return up(recs * d * 4) + up(recs * 2 * 4) + up((B + 1) * 4) + up(chunks * 16)
 
 
 def test_chunks_and_workspace_sizes(lib):

@@ -167,3 +167,25 @@ def test_chunked_prefill_full_size_sampled_rows():
     rows = sorted(set(rows))
     _check(w, got, _oracle(w, rows=rows), rows=rows)
     assert np.isfinite(as_f64(got)).all()
+
+
+def test_out_of_pool_block_ids_are_masked():
+    """A block id outside [0, num_blocks) below every query position is never read and its
+    16 positions are left out of every row's softmax: the result equals the attention with
+    that block removed from the sequence (positions after it move down by 16, which the
+    causal mask does not notice since the block lies before every query token)."""
+    import dataclasses
+    w = wl.prefill_custom(query_lens=[20, 5, 9], context_lens=[200, 70, 9], num_q_heads=8,
+                          num_kv_heads=2, head_dim=128, kv_dtype="bf16", out_dtype="f32", seed=4)
+    N = w.num_blocks
+    bad = w.block_tables.copy()
+    bad[0, 3] = N + 1          # positions 48..63, before the first query (180)
+    bad[1, 0] = -3             # positions 0..15, before the first query (65)
+    good = np.full_like(bad, -1)
+    good[0, :12] = np.delete(w.block_tables[0, :13], 3)
+    good[1, :4] = w.block_tables[1, 1:5]
+    good[2] = w.block_tables[2]
+    exp = dataclasses.replace(w, block_tables=good,
+                              context_lens=np.array([184, 54, 9], dtype=np.int32))
+    w_bad = dataclasses.replace(w, block_tables=bad)
+    _check(w_bad, _run(w_bad, _device(w_bad)), _oracle(exp), tol=2e-3)
