@@ -50,7 +50,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim, group, dtype combo)   */
   PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
   PA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                         */
-  PA_ERR_HIP = -7          /* the HIP runtime reported an error at launch              */
+  PA_ERR_HIP = -7,         /* the HIP runtime reported an error at launch              */
+  PA_ERR_SCRATCH = -11     /* pa_decode_noalloc: the call needs more than its static scratch */
 } pa_status_t;
 
 /* Shape of one decode call.
@@ -145,6 +146,25 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
                       const int32_t* block_tables, const int32_t* context_lens,
                       int32_t max_context_len, float scale, float k_scale, float v_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the static device scratch behind pa_decode_noalloc, one copy per GPU. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* pa_decode without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops that must
+ * not call hipMalloc, harnesses that forbid it. Arguments, results and errors are those
+ * of pa_decode (the same kernels run); the workspace is a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES inside the library, one copy on every GPU the library runs on,
+ * held until the process ends. A call whose workspace (pa_decode_workspace_bytes) would
+ * exceed it returns PA_ERR_SCRATCH and launches nothing. The scratch needs no clearing
+ * (every call writes what it reads), but all calls on one GPU share it: calls that overlap
+ * on one GPU (on different streams, or from threads without ordering) race and give
+ * undefined results; calls ordered on one stream are safe. */
+pa_status_t pa_decode_noalloc(const pa_decode_desc_t* desc, void* out, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t max_context_len, float scale, float k_scale,
+                              float v_scale, void* stream);
 
 /* Shape of one multi-token query call (pa_prefill).
  *   batch               B, sequences; 0 is allowed (no-op)

@@ -60,6 +60,8 @@ def load_library():
     lib.pa_decode_workspace_bytes.argtypes = [D, I32]
     lib.pa_decode.restype = I32
     lib.pa_decode.argtypes = [D, P, P, P, P, P, P, I32, F, F, F, P, SZ, P]
+    lib.pa_decode_noalloc.restype = I32
+    lib.pa_decode_noalloc.argtypes = [D, P, P, P, P, P, P, I32, F, F, F, P]
     lib.pa_decode_head_scales.restype = I32
     lib.pa_decode_head_scales.argtypes = [D, P, P, P, P, P, P, I32, F, P, P, P, SZ, P]
     lib.pa_prefill_head_scales.restype = I32
@@ -325,3 +327,28 @@ def pa_block_swap(dst_k, dst_v, src_k, src_v, src_dst_pairs, stream=None):
                            Hkv, d, bs, dtype_code(dst_k), _stream(stream))
     if st != 0:
         raise PaError(st, "pa_block_swap")
+
+
+def pa_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                      scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                      partition_size: int = 0, stream=None):
+    """pa_decode with the library's static scratch as workspace: allocates nothing (neither
+    here nor in the library). Calls overlapping on one GPU race (they share the scratch)."""
+    import torch
+    lib = load_library()
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool differ in shape or dtype")
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if context_lens.shape != (q.shape[0],):
+        raise ValueError("context_lens must be [batch]")
+    desc = make_desc(q, k_pool, block_tables, out, partition_size)
+    st = lib.pa_decode_noalloc(ctypes.byref(desc), _dev(out, "out"), _dev(q, "q"),
+                               _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                               _dev(block_tables, "block_tables", torch.int32),
+                               _dev(context_lens, "context_lens", torch.int32),
+                               int(max_context_len), float(scale), float(k_scale),
+                               float(v_scale), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_decode_noalloc")
+    return out

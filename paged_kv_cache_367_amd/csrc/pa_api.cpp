@@ -154,6 +154,8 @@ const char* pa_status_string(int32_t status) {
     case -8: return "not enough free or evictable KV blocks";      // pa_block_manager.h
     case -9: return "unknown sequence id, or the id is in use";   // pa_block_manager.h
     case -10: return "host memory ran out in the block manager";  // pa_block_manager.h
+    case PA_ERR_SCRATCH:
+      return "the call needs more workspace than pa_decode_noalloc's static scratch";
     default: return "unknown status";
   }
 }
@@ -174,14 +176,12 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc_t* desc, int32_t max_conte
 
 namespace {
 
-// pa_decode and pa_decode_head_scales: per-tensor scales, or (k_heads, v_heads) device
-// arrays of one scale per kv head (then k_scale = v_scale = 1 here)
-pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
-                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                        const int32_t* context_lens, int32_t max_context_len, float scale,
-                        float k_scale, float v_scale, const float* k_heads,
-                        const float* v_heads, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+// Checks of a decode call that need no workspace (PA_OK also for B = 0).
+pa_status_t check_decode_call(const pa_decode_desc_t* desc, void* out, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t max_context_len, float scale, float k_scale,
+                              float v_scale) {
   pa_status_t st = check_desc(desc, max_context_len);
   if (st != PA_OK) return st;
   if (desc->batch == 0) return PA_OK;
@@ -190,6 +190,21 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_ALIGN;
   if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// pa_decode and pa_decode_head_scales: per-tensor scales, or (k_heads, v_heads) device
+// arrays of one scale per kv head (then k_scale = v_scale = 1 here)
+pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
+                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t max_context_len, float scale,
+                        float k_scale, float v_scale, const float* k_heads,
+                        const float* v_heads, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  pa_status_t st = check_decode_call(desc, out, q, k_pool, v_pool, block_tables, context_lens,
+                                     max_context_len, scale, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (desc->batch == 0) return PA_OK;
   const Workspace ws = workspace_layout(desc, max_context_len);
   if (!workspace || workspace_bytes < ws.total) return PA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
@@ -272,6 +287,24 @@ pa_status_t pa_decode(const pa_decode_desc_t* desc, void* out, const void* q,
                       void* stream) {
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
                      scale, k_scale, v_scale, nullptr, nullptr, workspace, workspace_bytes,
+                     stream);
+}
+
+pa_status_t pa_decode_noalloc(const pa_decode_desc_t* desc, void* out, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t max_context_len, float scale, float k_scale,
+                              float v_scale, void* stream) {
+  pa_status_t st = check_decode_call(desc, out, q, k_pool, v_pool, block_tables, context_lens,
+                                     max_context_len, scale, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (desc->batch == 0) return PA_OK;
+  if (workspace_layout(desc, max_context_len).total > PA_NOALLOC_SCRATCH_BYTES)
+    return PA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (pa::noalloc_scratch(&ws) != hipSuccess) return PA_ERR_HIP;
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                     scale, k_scale, v_scale, nullptr, nullptr, ws, PA_NOALLOC_SCRATCH_BYTES,
                      stream);
 }
 

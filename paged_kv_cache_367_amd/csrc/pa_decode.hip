@@ -53,9 +53,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/paged_attention.h"
 #include "pa_device.h"
 #include "pa_launch.h"
+
+// Workspace of pa_decode_noalloc: one copy per GPU for the life of the process. In host
+// code this name stands for the device symbol only; kernels get the device address that
+// noalloc_scratch looks up.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
 
 namespace pa {
 namespace {
@@ -1161,6 +1169,31 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, int out_dtype, int head_dim,
       return dispatch_dim<PA_FP8_E4M3, PA_BF16, PA_F32>(head_dim, group, args, nw, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// The current device's address of `scratch`: hipGetSymbolAddress once per device, with
+// that device current, kept for later calls.
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_merge(int out_dtype, int head_dim, int group, const MergeArgs& args,

@@ -168,6 +168,10 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, int out_dtype, int head_dim,
 hipError_t launch_merge(int out_dtype, int head_dim, int group, const MergeArgs& args,
                         hipStream_t stream);
 
+// Device address of the current GPU's copy of the static decode scratch
+// (PA_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_prefill(int q_dtype, int kv_dtype, int out_dtype, int head_dim, int group,
                           const PrefillArgs& args, hipStream_t stream);
 

@@ -217,3 +217,21 @@ def test_head_scale_entry_points_reject_before_launch(lib):
     assert w8(z, p) == -1 and w8(p, odd) == -6
     assert w8(p, p, d=36) == -4                     # head_dim not a multiple of 8
     assert w8(z, z, n=0) == 0
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """pa_decode_noalloc checks the workspace a call needs against its static scratch
+    (PA_NOALLOC_SCRATCH_BYTES, 64 MiB) before touching the GPU."""
+    p = ctypes.c_void_p(0x10000)
+    # 200 sequences of up to 1024 tokens in 16-token partitions: 13 056 chunks of records
+    d = _desc(batch=200, max_blocks_per_seq=64, partition_size=16)
+    assert pa.pa_decode_workspace_bytes(d, 1024) > 64 << 20
+    assert lib.pa_decode_noalloc(ctypes.byref(d), p, p, p, p, p, p, 1024, 0.088, 1.0, 1.0,
+                                 None) == -11
+    assert "static scratch" in pa.pa_status_string(-11)
+    # and the ordinary argument checks come first
+    assert lib.pa_decode_noalloc(ctypes.byref(d), None, p, p, p, p, p, 1024, 0.088, 1.0, 1.0,
+                                 None) == -1
+    d0 = _desc(batch=0)
+    assert lib.pa_decode_noalloc(ctypes.byref(d0), None, None, None, None, None, None, 16,
+                                 0.088, 1.0, 1.0, None) == 0
