@@ -14,9 +14,12 @@ Output: one JSON line on stdout. `value` is KV-read GB/s over the whole step
 token each) per second for this one attention layer. `roofline` describes the decode
 launch (main + merge kernels), timed with HIP events on the stream it runs on (mean, and
 p10/p50/p90 over the timed steps), and sets its bandwidth against the 8 TB/s peak and
-against a copy ceiling measured on the same GPU after the timed region (a 1 GiB device
-copy, bytes read plus written). `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the same workload.
+against a read ceiling measured on the same GPU after the timed region (pa_stream_read
+over 4 GiB: the library's streaming-read kernel, the best a read-only kernel does here;
+a 1 GiB device copy, bytes read plus written, is reported beside it). With the default
+workload (3) the Llama-2-7B fp16, prefix-sharing and long-context fp8 workloads (2, 4, 5)
+are measured the same way afterwards and reported under `other_workloads`.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the main workload.
 
 With --path prefill the step is one chunked-prefill step instead (workload.chunked_prefill:
 16 prompts x 512 new tokens over contexts of up to 8192): the slot write of the chunk's
@@ -102,6 +105,27 @@ def copy_ceiling_gbs(mib: int = 1024, reps: int = 5) -> float:
         best = min(best, e0.elapsed_time(e1))
     del src, dst
     return 2 * n / (best * 1e-3) / 1e9
+
+
+def read_ceiling_gbs(gib: int = 4, reps: int = 5) -> float:
+    """Measured read-only HBM ceiling on this GPU: pa_stream_read over `gib` GiB (far
+    larger than the caches), bytes read per second, best of `reps`."""
+    import torch
+    import paged_kv_cache_367_amd as pa
+    n = gib << 30
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa.pa_stream_read(buf, sink)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pa.pa_stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del buf, sink
+    return n / (best * 1e-3) / 1e9
 
 
 def cpu_baseline(w, gpu_out, k_after, v_after, budget_s: float):
@@ -420,6 +444,10 @@ def main() -> int:
     ap.add_argument("--path", choices=["decode", "prefill", "swap", "manager"], default="decode",
                     help="decode (the default step), one chunked-prefill step, a block swap "
                          "to pinned host memory and back, or the host block manager")
+    ap.add_argument("--extra-configs", default=None,
+                    help="decode: other workloads measured after the main one and reported "
+                         "under other_workloads (comma list, or 'none'; default 2,4,5 with "
+                         "the default --config 3, else none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -473,6 +501,66 @@ def main() -> int:
     log(f"workload {w.name}: B={w.batch} tokens={w.total_tokens} kv_bytes={w.kv_bytes} "
         f"pool_blocks={w.num_blocks} ({time.perf_counter() - t0:.1f} s)")
     part = args.partition_size if args.partition_size is not None else w.partition_size
+    m = measure_decode(w, part, args.steps, args.warmup, args.replicas)
+    read_gbs = read_ceiling_gbs()
+    copy_gbs = copy_ceiling_gbs()
+    log(f"ceilings on this GPU: streaming read {read_gbs:.0f} GB/s, device copy "
+        f"{copy_gbs:.0f} GB/s (read + write)")
+    record = decode_record(w, part, m, args)
+    rf = record["roofline"]
+    rf["read_ceiling_gbs"] = read_gbs
+    rf["frac_of_read_ceiling"] = rf["achieved"] / read_gbs
+    rf["copy_ceiling_gbs"] = copy_gbs
+    extra_arg = args.extra_configs if args.extra_configs is not None else \
+        ("2,4,5" if args.config == 3 else "none")
+    extra = [] if extra_arg in ("", "none") else \
+        [int(x) for x in extra_arg.split(",") if int(x) != args.config]
+    if args.batch is not None or args.context is not None:
+        extra = []
+    if extra:
+        record["other_workloads"] = []
+        for idx in extra:
+            log(f"building workload {idx}")
+            wx = wl.make(idx)
+            mx = measure_decode(wx, wx.partition_size, min(args.steps, 20), args.warmup,
+                                args.replicas)
+            rx = decode_record(wx, wx.partition_size, mx, args)
+            sub = {k: rx[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s",
+                                      "hbm_frac", "dtype", "steps")}
+            sub["config"] = rx["config"]
+            sub["roofline"] = {k: rx["roofline"][k] for k in (
+                "kernel", "bound", "achieved", "peak", "unit", "frac", "traffic", "launch_ms",
+                "launch_ms_p10_p50_p90", "algorithmic_bytes_per_launch")}
+            sub["roofline"]["frac_of_read_ceiling"] = rx["roofline"]["achieved"] / read_gbs
+            record["other_workloads"].append(sub)
+            del mx
+            torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: applying the step's writes to host pools")
+        k_after, v_after = w.k_pool, w.v_pool
+        if w.copy_pairs is not None:
+            k_after = oracle.block_copy_ref(k_after, w.copy_pairs)
+            v_after = oracle.block_copy_ref(v_after, w.copy_pairs)
+        if w.slot_mapping is not None:
+            k_after = oracle.cache_write_ref(k_after, w.k_new, w.slot_mapping)
+            v_after = oracle.cache_write_ref(v_after, w.v_new, w.slot_mapping)
+        log(f"cpu baseline: timing the oracle (~{args.cpu_budget_s:.0f} s)")
+        record["cpu_baseline"] = cpu_baseline(w, m["out"], k_after, v_after, args.cpu_budget_s)
+        log(f"cpu baseline: {record['cpu_baseline']['sample']}")
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def measure_decode(w, part, steps, warmup, replicas):
+    """Time `steps` decode steps (copy-on-write copies, slot writes, pa_decode) of workload
+    w after `warmup` untimed ones, the pool replicated `replicas` times (step i uses
+    replica i % replicas). Returns the step time, the pa_decode launch times (HIP events
+    on the stream the kernels run on) and the last output as float64 numpy."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_367_amd as pa
 
     def dev(a, kind=None):
         a = np.ascontiguousarray(a)
@@ -482,7 +570,7 @@ def main() -> int:
 
     q = dev(w.q, w.q_dtype)
     tables, lens = dev(w.block_tables), dev(w.context_lens)
-    R = max(1, args.replicas)
+    R = max(1, replicas)
     ks = [dev(w.k_pool, w.kv_dtype) for _ in range(R)]
     vs = [dev(w.v_pool, w.kv_dtype) for _ in range(R)]
     slots = dev(w.slot_mapping) if w.slot_mapping is not None else None
@@ -496,11 +584,10 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     chunks = pa.pa_decode_max_chunks(desc, w.max_context_len)
     torch.cuda.synchronize()
-    log(f"resident: {R} pool replicas, workspace {ws_bytes} B, up to {chunks} work chunks")
-
-    n_ev = args.steps
-    dec0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    dec1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    log(f"{w.name}: resident: {R} pool replicas, workspace {ws_bytes} B, up to {chunks} "
+        f"work chunks")
+    dec0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    dec1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
 
     def step(i, timed):
         r = i % R
@@ -515,32 +602,38 @@ def main() -> int:
         if timed:
             dec1[i].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, True)
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = start.elapsed_time(end) / steps
     dec_ms = [a.elapsed_time(b) for a, b in zip(dec0, dec1)]
     dec_avg = sum(dec_ms) / len(dec_ms)
-    dec_sorted = sorted(dec_ms)
-    pct = lambda f: dec_sorted[min(len(dec_sorted) - 1, int(f * len(dec_sorted)))]
-    copy_gbs = copy_ceiling_gbs()
-    log(f"timed {args.steps} steps: {ms:.4f} ms/step, decode launch avg {dec_avg:.4f} ms "
+    srt = sorted(dec_ms)
+    pct = lambda f: srt[min(len(srt) - 1, int(f * len(srt)))]
+    log(f"{w.name}: timed {steps} steps: {ms:.4f} ms/step, decode launch avg {dec_avg:.4f} ms "
         f"(min {min(dec_ms):.4f}, max {max(dec_ms):.4f})")
+    res = {"ms": ms, "launch_ms": dec_avg, "pct": [pct(0.1), pct(0.5), pct(0.9)],
+           "chunks": chunks, "replicas": R, "steps": steps,
+           "out": out.to(torch.float64).cpu().numpy()}
+    del ks, vs, ws
+    return res
 
-    gbs = w.kv_bytes / (ms * 1e-3) / 1e9
-    achieved = w.kv_bytes / (dec_avg * 1e-3) / 1e9
-    record = {
-        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None,
+
+def decode_record(w, part, m, args):
+    """The JSON record of one measured decode workload."""
+    gbs = w.kv_bytes / (m["ms"] * 1e-3) / 1e9
+    achieved = w.kv_bytes / (m["launch_ms"] * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": m["steps"],
+        "warmup": args.warmup, "ms_per_step": m["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
         "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[w.kv_dtype],
         "data": "synthetic (seeded, workload.py)",
         "config": {
@@ -548,37 +641,20 @@ def main() -> int:
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "accumulate": "f32",
             "context_tokens": w.total_tokens, "max_context_len": w.max_context_len,
-            "kv_bytes_per_step": w.kv_bytes, "partition_size": part, "max_work_chunks": chunks,
-            "pool_replicas": R, "seed": w.seed,
+            "kv_bytes_per_step": w.kv_bytes, "partition_size": part,
+            "max_work_chunks": m["chunks"], "pool_replicas": m["replicas"], "seed": w.seed,
         },
-        "tokens_per_s": w.batch / (ms * 1e-3),
+        "tokens_per_s": w.batch / (m["ms"] * 1e-3),
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "roofline": {
             "kernel": "pa_decode (decode_kernel + merge kernel)", "bound": "hbm",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
-            "launch_ms": dec_avg, "algorithmic_bytes_per_launch": w.kv_bytes,
-            "launch_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-            "copy_ceiling_gbs": copy_gbs, "frac_of_copy_ceiling": achieved / copy_gbs,
+            "launch_ms": m["launch_ms"], "algorithmic_bytes_per_launch": w.kv_bytes,
+            "launch_ms_p10_p50_p90": m["pct"],
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        import oracle
-        log("cpu baseline: applying the step's writes to host pools")
-        k_after, v_after = w.k_pool, w.v_pool
-        if w.copy_pairs is not None:
-            k_after = oracle.block_copy_ref(k_after, w.copy_pairs)
-            v_after = oracle.block_copy_ref(v_after, w.copy_pairs)
-        if w.slot_mapping is not None:
-            k_after = oracle.cache_write_ref(k_after, w.k_new, w.slot_mapping)
-            v_after = oracle.cache_write_ref(v_after, w.v_new, w.slot_mapping)
-        gpu_out = out.to(torch.float64).cpu().numpy()
-        log(f"cpu baseline: timing the oracle (~{args.cpu_budget_s:.0f} s)")
-        record["cpu_baseline"] = cpu_baseline(w, gpu_out, k_after, v_after, args.cpu_budget_s)
-        log(f"cpu baseline: {record['cpu_baseline']['sample']}")
-    print(json.dumps(record), flush=True)
-    return 0
 
 
 if __name__ == "__main__":

@@ -321,6 +321,16 @@ pa_status_t pa_block_swap(void* dst_k_pool, void* dst_v_pool, int32_t dst_num_bl
                           const int64_t* src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t kv_dtype, void* stream);
 
+/* Measurement aid, not part of the attention path: reads `bytes` of device memory at `src`
+ * once (each of `workgroups` workgroups of 256 threads streams a contiguous slab with
+ * eight 16-byte non-temporal loads in flight per thread; 0 = 8 workgroups per compute
+ * unit) and writes at most one 32-bit word to `sink`, so that its time
+ * gives the read-only HBM bandwidth that a kernel which only reads (the decode) can reach
+ * on this GPU. src and sink are device pointers, src 16-byte aligned, bytes a multiple of
+ * 16. */
+pa_status_t pa_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,6 @@ from .binding import (  # noqa: F401
     load_library,
     pa_abi_version, pa_status_string, pa_decode_max_chunks, decode_workspace, pa_decode_workspace_bytes,
     pa_decode, pa_decode_noalloc, pa_prefill, pa_cache_write, pa_cache_write_fp8, pa_block_copy,
-    pa_block_swap,
+    pa_block_swap, pa_stream_read,
 )
 from .block_manager import BlockManager, PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ  # noqa: F401

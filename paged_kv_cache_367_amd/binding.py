@@ -78,6 +78,8 @@ def load_library():
     lib.pa_cache_write_fp8.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F, F, P]
     lib.pa_block_swap.restype = I32
     lib.pa_block_swap.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, I32, I32, P]
+    lib.pa_stream_read.restype = I32
+    lib.pa_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.pa_block_copy.restype = I32
     lib.pa_block_copy.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P]
     _LIB = lib
@@ -352,3 +354,12 @@ def pa_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     if st != 0:
         raise PaError(st, "pa_decode_noalloc")
     return out
+
+
+def pa_stream_read(buf, sink, workgroups: int = 0, stream=None):
+    """Read every byte of the GPU tensor `buf` once (a read-only bandwidth reference);
+    `sink` is a GPU tensor of at least 4 bytes."""
+    st = load_library().pa_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                       _dev(sink, "sink"), int(workgroups), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_stream_read")

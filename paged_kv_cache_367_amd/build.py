@@ -21,7 +21,7 @@ ARCH = "gfx950"
 LIB = os.path.join(PKG, "libpa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["csrc/pa_api.cpp", "csrc/pa_decode.hip", "csrc/pa_prefill.hip",
-           "csrc/pa_cache_ops.hip", "csrc/pa_block_manager.cpp"]
+           "csrc/pa_cache_ops.hip", "csrc/pa_block_manager.cpp", "csrc/pa_measure.hip"]
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -536,6 +536,19 @@ pa_status_t pa_block_copy(void* k_pool, void* v_pool, const int64_t* src_dst_pai
   return PA_OK;
 }
 
+pa_status_t pa_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                           void* stream) {
+  if (workgroups < 0) return PA_ERR_SHAPE;
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink) return PA_ERR_NULL;
+  if (!aligned(src, 16) || bytes % 16 != 0 || !aligned(sink, 4)) return PA_ERR_ALIGN;
+  const int wg = workgroups > 0 ? workgroups : device_cus() * 8;
+  if (pa::launch_stream_read(src, bytes, sink, wg, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
 pa_status_t pa_block_swap(void* dst_k_pool, void* dst_v_pool, int32_t dst_num_blocks,
                           const void* src_k_pool, const void* src_v_pool, int32_t src_num_blocks,
                           const int64_t* src_dst_pairs, int32_t num_pairs, int32_t num_kv_heads,

@@ -55,6 +55,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/paged_attention.h"
 #include "pa_device.h"
@@ -316,6 +317,8 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   constexpr int PBUF = kBlockTokens * G + 8;    // p of one block (+ alpha[8]), one wave
 
   __shared__ int s_lens[kMaxBatch];        // clamped context length per sequence
+  __shared__ int s_first[kMaxBatch];       // first block id of each sequence
+  __shared__ uint8_t s_shr[kMaxBatch];     // the sequence probably shares blocks
   __shared__ int s_pre[kMaxBatch + 1];     // blocks before each sequence
   __shared__ int s_wsum[kMaxGroupWaves];
   __shared__ float s_p[kMaxGroupWaves][2 * PBUF];
@@ -332,13 +335,20 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 
   // ---- 1. lengths and block prefix sums of the whole batch, in LDS. Thread t owns the
   // sequences [t*K, t*K + K). Every workgroup computes them; workgroup 0 also stores the
-  // prefix sums for the merge.
+  // prefix sums for the merge. The first block id of every sequence rides along (same
+  // memory round trip): a sequence whose first block is its neighbour's (parallel samples
+  // or beam forks of one prompt) shares blocks, and so does every sequence of a batch
+  // that references more blocks than the pool holds. A workgroup that visits such a
+  // sequence keeps the cached policy for its K/V loads, so that the other readers of a
+  // shared block find it in the caches; the others stream K/V, read once, past them.
   const int K = (B + nthr - 1) / nthr;
   const int b_lo = min(B, tid * K), b_hi = min(B, b_lo + K);
   int mine = 0;
   for (int b = b_lo; b < b_hi; ++b) {
     const int L = clamp_len(a.context_lens[b], cap);
+    const int f = a.block_tables[(size_t)b * a.max_blocks_per_seq];
     s_lens[b] = L;
+    s_first[b] = L > 0 ? f : -1 - b;        // distinct from every id when empty
     mine += nblocks(L);
   }
   int incl = mine;
@@ -356,11 +366,15 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     total += x;
   }
   {
+    const bool oversubscribed = total > a.num_blocks;
     int c = before + incl - mine;                    // blocks of sequences before b_lo
     for (int b = b_lo; b < b_hi; ++b) {
       s_pre[b] = c;
       if (blockIdx.x == 0) a.prefix[b] = c;
       c += nblocks(s_lens[b]);
+      const int f = s_first[b];
+      s_shr[b] = oversubscribed || (b > 0 && s_first[b - 1] == f) ||
+                 (b + 1 < B && s_first[b + 1] == f);
     }
     if (tid == 0) {
       s_pre[B] = total;
@@ -389,13 +403,16 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   // test form a prefix of [0, B): count them with two wave ballots, first over 64 evenly
   // spaced samples, then inside the stretch the count ends in.
   const int SPAN = (B + kWave - 1) / kWave;
-  auto locate = [&](int u) {
+  auto seq_of = [&](int u) -> int {
     const int b1 = lane * SPAN;
     const bool p1 = b1 < B && HGC * s_pre[b1] <= u;
     const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(p1)) - 1;
     const int b2 = k * SPAN + lane;
     const bool p2 = lane < SPAN && b2 < B && HGC * s_pre[b2] <= u;
-    const int lo = uni(k * SPAN + __builtin_popcountll(__builtin_amdgcn_ballot_w64(p2)) - 1);
+    return uni(k * SPAN + __builtin_popcountll(__builtin_amdgcn_ballot_w64(p2)) - 1);
+  };
+  auto locate = [&](int u) {
+    const int lo = seq_of(u);
     wb = lo;
     wL = uni(s_lens[lo]);
     wnb = nblocks(wL);
@@ -437,6 +454,15 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   if (!cg.fixed && chunk_begin(cg, rng) == chunk_end(cg, rng))
     note_header(rng, false, 0);   // an empty chunk ends no segment
   enter(next_nonempty(rng * cg.per_wg - 1));
+  // the workgroup's K/V loads keep the cached policy when any sequence it visits probably
+  // shares blocks, and stream otherwise (decided once, so the loop carries no branch)
+  bool wg_shared = false;
+  if (cur >= 0) {
+    const int b_last = seq_of((int)chunk_end(cg, c_last) - 1);
+    bool any = false;
+    for (int b = wb + lane; b <= b_last; b += kWave) any |= s_shr[b] != 0;
+    wg_shared = __builtin_amdgcn_ballot_w64(any) != 0;
+  }
   // default split: sequences of length 0 own no units; workgroup r writes the zero
   // outputs of sequences r, r + W, ... (with fixed partitions the merge does)
   if (!cg.fixed) {
@@ -501,8 +527,9 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   // unit opens a piece. Always the same instructions, so wait counts stay static.
   // A block id outside [0, num_blocks) is never dereferenced: its unit keeps rem = 0, so
   // all 16 of its tokens are masked out of the softmax like rows past L.
-  auto issue = [&](UnitMeta& m, uint32_t idv, u32x4(&kb)[NL], VT(&vb)[NLV],
+  auto issue = [&](auto pol, UnitMeta& m, uint32_t idv, u32x4(&kb)[NL], VT(&vb)[NLV],
                    u32x4(&qs)[QPL]) {
+    constexpr int POL = decltype(pol)::value;
     const int pid = __builtin_amdgcn_readfirstlane((int)idv);
     const bool valid = (m.flags() & kValid) && (unsigned)pid < (unsigned)a.num_blocks;
     if (!valid) m.bf &= 0x00ffffff;
@@ -517,10 +544,11 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + qo, wantq ? (uint32_t)QBYTES : 0u);
 #pragma unroll
     for (int i = 0; i < QPL; ++i) qs[i] = buf_load16(rq, (uint32_t)(lane + kWave * i) * 16u);
+    // K and V with the workgroup's cache policy (streaming unless blocks are shared)
 #pragma unroll
-    for (int s = 0; s < NL; ++s) kb[s] = buf_load16(rk, koff + s * 64);
+    for (int s = 0; s < NL; ++s) kb[s] = buf_load16<POL>(rk, koff + s * 64);
 #pragma unroll
-    for (int i = 0; i < NLV; ++i) vb[i] = VChunk<VB>::load(rv, voff + i * vstep);
+    for (int i = 0; i < NLV; ++i) vb[i] = VChunk<VB>::template load<POL>(rv, voff + i * vstep);
   };
 
   // ---- 4. running state of the current piece
@@ -795,52 +823,59 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   // x % R). Step k first issues the K/V loads of unit k + NBUF into the slot unit k - 1
   // has just left (its block id was loaded R steps earlier) and the id load of unit
   // k + NBUF + R, then computes unit k: NBUF units stay in flight while one is computed.
-  // The ring is unrolled so that every slot index is a constant.
+  // The ring is unrolled so that every slot index is a constant. It is compiled once per
+  // cache policy of the K/V loads.
   constexpr int R = NBUF + 1;
-  u32x4 kb[R][NL];
-  VT vb[R][NLV];
-  u32x4 qs[R][QPL];
-  uint32_t idv[R];
-  UnitMeta mk[R], mi[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    mi[u] = snapshot();
-    idv[u] = load_id(mi[u]);
-    advance();
-  }
-#pragma unroll
-  for (int u = 0; u < NBUF; ++u) {
-    mk[u] = mi[u];
-    issue(mk[u], idv[u], kb[u], vb[u], qs[u]);
-    mi[u] = snapshot();
-    idv[u] = load_id(mi[u]);
-    advance();
-  }
-  if (!cg.fixed && wave == 0 && lane == 0) {
-    int4 hd = make_int4(-1, 0, 0, 0);
-    if (hdr_b >= 0) {
-      const int cf = chunk_of(cg, hdr_sseg);
-      hd = make_int4(hdr_b, hdr_hg, cf, chunk_begin(cg, cf) < hdr_sseg ? 1 : 0);
-    }
-    *reinterpret_cast<int4*>(a.chunk_hdr + 4 * hdr_c) = hd;
-  }
-  // every wave sees the same chunks, so the loop ends at the same step in all of them
-  for (;;) {
+  auto stream = [&](auto pol) {
+    u32x4 kb[R][NL];
+    VT vb[R][NLV];
+    u32x4 qs[R][QPL];
+    uint32_t idv[R];
+    UnitMeta mk[R], mi[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int si = (u + NBUF) % R;   // slot of unit k + NBUF (= slot of unit k - 1)
-      mk[si] = mi[si];
-      issue(mk[si], idv[si], kb[si], vb[si], qs[si]);
-      mi[si] = snapshot();
-      idv[si] = load_id(mi[si]);
+      mi[u] = snapshot();
+      idv[u] = load_id(mi[u]);
       advance();
-      compute(mk[u], kb[u], vb[u], qs[u], pw + (u & 1) * PBUF);
     }
-    bool busy = cur >= 0;
 #pragma unroll
-    for (int u = 0; u < R; ++u) busy |= ((mk[u].flags() | mi[u].flags()) & kValid) != 0;
-    if (!busy) break;
-  }
+    for (int u = 0; u < NBUF; ++u) {
+      mk[u] = mi[u];
+      issue(pol, mk[u], idv[u], kb[u], vb[u], qs[u]);
+      mi[u] = snapshot();
+      idv[u] = load_id(mi[u]);
+      advance();
+    }
+    if (!cg.fixed && wave == 0 && lane == 0) {
+      int4 hd = make_int4(-1, 0, 0, 0);
+      if (hdr_b >= 0) {
+        const int cf = chunk_of(cg, hdr_sseg);
+        hd = make_int4(hdr_b, hdr_hg, cf, chunk_begin(cg, cf) < hdr_sseg ? 1 : 0);
+      }
+      *reinterpret_cast<int4*>(a.chunk_hdr + 4 * hdr_c) = hd;
+    }
+    // every wave sees the same chunks, so the loop ends at the same step in all of them
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int si = (u + NBUF) % R;   // slot of unit k + NBUF (= slot of unit k - 1)
+        mk[si] = mi[si];
+        issue(pol, mk[si], idv[si], kb[si], vb[si], qs[si]);
+        mi[si] = snapshot();
+        idv[si] = load_id(mi[si]);
+        advance();
+        compute(mk[u], kb[u], vb[u], qs[u], pw + (u & 1) * PBUF);
+      }
+      bool busy = cur >= 0;
+#pragma unroll
+      for (int u = 0; u < R; ++u) busy |= ((mk[u].flags() | mi[u].flags()) & kValid) != 0;
+      if (!busy) break;
+    }
+  };
+  if (wg_shared)
+    stream(std::integral_constant<int, kCached>{});
+  else
+    stream(std::integral_constant<int, kStream>{});
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

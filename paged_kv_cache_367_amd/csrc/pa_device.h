@@ -59,11 +59,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// Cache policy of a load: kCached, or kStream (the nt bit: data read once, which the caches
+// should not keep; streaming reads reach more HBM bandwidth with it).
+constexpr int kCached = 0, kStream = 2;
+template <int POL = kCached>
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, POL));
 }
+template <int POL = kCached>
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, POL));
 }
 
 // fp32 -> bf16, round to nearest even (the hardware conversion of CDNA4)
@@ -105,29 +110,33 @@ __device__ __forceinline__ float xrow_sum(float x) {
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
+template <int POL = kCached>
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, POL);
 }
 
-// Loads of 16, 8 or 4 bytes per lane through a buffer descriptor.
+// Loads of 16, 8 or 4 bytes per lane through a buffer descriptor, with cache policy POL.
 template <int BYTES> struct VChunk;
 template <> struct VChunk<16> {
   using type = u32x4;
+  template <int POL = kCached>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-    return buf_load16(r, o);
+    return buf_load16<POL>(r, o);
   }
 };
 template <> struct VChunk<8> {
   using type = u32x2;
+  template <int POL = kCached>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-    return buf_load8(r, o);
+    return buf_load8<POL>(r, o);
   }
 };
 template <> struct VChunk<4> {
   using type = u32x1;
+  template <int POL = kCached>
   static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
     u32x1 v;
-    v[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)o, 0, 0);
+    v[0] = buf_load4<POL>(r, o);
     return v;
   }
 };

@@ -187,6 +187,8 @@ hipError_t launch_cache_write_fp8(void* k_pool, void* v_pool, const void* k_new,
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int64_t* pairs,
                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                              hipStream_t stream);
+hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int workgroups,
+                              hipStream_t stream);
 hipError_t launch_block_swap(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k,
                              const void* src_v, int32_t src_blocks, const int64_t* pairs,
                              int32_t num_pairs, int64_t block_bytes, hipStream_t stream);
