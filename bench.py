@@ -448,6 +448,9 @@ def main() -> int:
                     help="decode: other workloads measured after the main one and reported "
                          "under other_workloads (comma list, or 'none'; default 2,4,5 with "
                          "the default --config 3, else none)")
+    ap.add_argument("--latency", action="store_true",
+                    help="decode: also time pa_decode calls replayed from a HIP graph (GPU time "
+                         "per call without host gaps; what small batches should be judged by)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -508,6 +511,12 @@ def main() -> int:
         f"{copy_gbs:.0f} GB/s (read + write)")
     record = decode_record(w, part, m, args)
     rf = record["roofline"]
+    if args.latency:
+        us, same = graph_latency(w, part)
+        rf["graph_launch_us"] = us
+        rf["graph_replays_match_eager"] = same
+        log(f"{w.name}: pa_decode from a HIP graph: {us:.1f} us per call (replays equal the "
+            f"eager output: {same})")
     rf["read_ceiling_gbs"] = read_gbs
     rf["frac_of_read_ceiling"] = rf["achieved"] / read_gbs
     rf["copy_ceiling_gbs"] = copy_gbs
@@ -535,6 +544,14 @@ def main() -> int:
             record["other_workloads"].append(sub)
             del mx
             torch.cuda.empty_cache()
+    if extra:
+        # the tiny fp32 workload is latency-bound: GPU time per call from a HIP graph
+        wt = wl.make(1)
+        us, same = graph_latency(wt, 0)
+        record["tiny_workload_latency"] = {
+            "workload": wt.name, "graph_launch_us": us, "graph_replays_match_eager": same,
+            "batch": wt.batch, "context_tokens": wt.total_tokens}
+        log(f"{wt.name}: pa_decode from a HIP graph: {us:.1f} us per call")
     if not args.no_cpu_baseline:
         import oracle
         log("cpu baseline: applying the step's writes to host pools")
@@ -624,6 +641,59 @@ def measure_decode(w, part, steps, warmup, replicas):
            "out": out.to(torch.float64).cpu().numpy()}
     del ks, vs, ws
     return res
+
+
+def graph_latency(w, part, launches=40, reps=5, replicas=3):
+    """GPU time of one pa_decode call without host gaps: `launches` calls (cycling over the
+    pool replicas) captured in one HIP graph, replayed `reps` times, (replay time) /
+    launches, best of the replays. Small batches take less GPU time per call than the host
+    takes to submit one, so events around single calls would time the host. Returns
+    (microseconds per call, output of the replays equals the eager output)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_367_amd as pa
+
+    def dev(a, kind=None):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if kind == "bf16" \
+            else torch.from_numpy(a)
+        return t.cuda()
+
+    q = dev(w.q, w.q_dtype)
+    tables, lens = dev(w.block_tables), dev(w.context_lens)
+    R = max(1, replicas)
+    ks = [dev(w.k_pool, w.kv_dtype) for _ in range(R)]
+    vs = [dev(w.v_pool, w.kv_dtype) for _ in range(R)]
+    out_dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.out_dtype]
+    out = torch.empty(tuple(w.q.shape), dtype=out_dtype, device="cuda")
+    desc = pa.binding.make_desc(q, ks[0], tables, out, part)
+    ws = torch.empty(max(pa.pa_decode_workspace_bytes(desc, w.max_context_len), 16),
+                     dtype=torch.uint8, device="cuda")
+
+    def call(r):
+        pa.pa_decode(out, q, ks[r], vs[r], tables, lens, w.max_context_len, w.scale,
+                     w.k_scale, w.v_scale, workspace=ws, partition_size=part)
+
+    call(0)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            call(i % R)
+    best, same = float("inf"), True
+    for _ in range(reps):
+        out.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+        same &= bool(torch.equal(out, eager))
+    del g, ks, vs, ws
+    return best * 1e3 / launches, same
 
 
 def decode_record(w, part, m, args):

@@ -265,9 +265,13 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
     const int64_t segments = (int64_t)(desc->num_kv_heads / nw) * desc->batch;
     const int64_t max_units = segments * seq_blocks;
     m.chunk_merge = (4 * segments >= W && max_units >= 8 * (int64_t)W) ? 1 : 0;
-    // a segment holds at most seq_blocks units, so at most that many pieces (chunks can
-    // be shorter than a partition when the batch has few units)
-    m.max_pieces = (int32_t)(seq_blocks < INT32_MAX ? seq_blocks : INT32_MAX);
+    // pieces a segment typically has (it sizes the per-segment merge's workgroups; any
+    // count is handled): the chunks a call can have shared among the segments, plus one,
+    // and never more than a segment's blocks
+    const int64_t pu = part_units(desc);
+    const int64_t chunks = pu > 0 ? W + (segments * seq_blocks + pu - 1) / pu : W;
+    const int64_t pieces = (chunks + segments - 1) / (segments > 0 ? segments : 1) + 1;
+    m.max_pieces = (int32_t)(pieces < seq_blocks ? pieces : seq_blocks);
   }
   m.v_scale = v_scale;
   m.v_head_scales = v_heads;

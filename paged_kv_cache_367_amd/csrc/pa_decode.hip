@@ -916,27 +916,31 @@ __device__ __forceinline__ void load_floats(const float* p, float (&x)[N]) {
 // out = v_scale * sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), with v_scale the
 // per-tensor scale or kv head g's own.
 // Also writes zeros for sequences of length 0 (they own no units). One workgroup of MW
-// waves per (kv head, sequence); lane i of a wave handles EPL consecutive outputs of
-// query head h. Wave w folds pieces w, w + MW, ... into a running (M, L, A) with the
-// online rule, UNROLL pieces per memory round trip (all of a 32k-token sequence's
-// 512-token partitions in one trip); the MW partial results are then combined through
-// LDS.
-// waves of a fixed-partition merge workgroup: 16, or 8 when G * D = 1024 (the partial
-// results then still fit 32 KB of LDS)
-template <int G, int D>
-constexpr int merge_waves() { return G * D >= 1024 ? 8 : 16; }
+// waves per (kv head, sequence, one of NS slices of the head dimension): a few long sequences
+// still spread the merge over many CUs. Lane i of a wave handles EPL consecutive outputs
+// of query head h within the slice. Wave w folds pieces w, w + MW, ... into a running
+// (M, L, A) with the online rule, UNROLL pieces per memory round trip (more when a lane
+// holds fewer outputs: all of a 32k-token sequence's 256 one-block pieces in one trip
+// with NS = 8); the MW partial results are then combined through LDS.
+// waves of a fixed-partition merge workgroup: 16, or 8 when a slice's G * D / NS outputs
+// are 1024 (the partial results then still fit 32 KB of LDS)
+template <int G, int D, int NS>
+constexpr int merge_waves() { return G * D / NS >= 1024 ? 8 : 16; }
 
-template <int OT, int D, int G>
+template <int OT, int D, int G, int NS>
 __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
-  constexpr int EPL = G * D / kWave;
-  constexpr int MWMAX = merge_waves<G, D>(), UNROLL = 4;
-  static_assert(EPL >= 1 && D % EPL == 0, "merge layout");
+  constexpr int DS = D / NS;               // dims of the slice
+  constexpr int EPL = G * DS / kWave;
+  constexpr int MWMAX = merge_waves<G, D, NS>();
+  constexpr int UNROLL = EPL >= 8 ? 4 : (EPL >= 4 ? 8 : 16);   // as the host assumes
+  static_assert(EPL >= 1 && DS % EPL == 0, "merge layout");
   __shared__ float s_ml[MWMAX][G][2];
-  __shared__ float s_acc[MWMAX][G * D];
-  const int MW = blockDim.x / kWave;       // 4, or MWMAX when a segment may have > 16 pieces
+  __shared__ float s_acc[MWMAX][G * DS];
+  const int MW = blockDim.x / kWave;       // 4 .. MWMAX, from the pieces a segment typically has
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int h = lane * EPL / D, d0 = (lane * EPL) % D;
+  const int g = blockIdx.x / NS, b = blockIdx.y;
+  const int h = lane * EPL / DS, d0 = (int)(blockIdx.x % NS) * DS + (lane * EPL) % DS;
+  const int dl = (lane * EPL) % DS;        // position within the slice
   const size_t o = ((size_t)b * a.num_q_heads + (size_t)g * G + h) * D + d0;
   const int c0 = a.prefix[b], nb = a.prefix[b + 1] - c0, total = a.prefix[a.batch];
   if (nb == 0) {
@@ -968,8 +972,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
   // records of chunk c: its first piece is in slot 0, its last (if different) in slot
   // 1; only chunk cf can hold the segment as its last piece
   const int slot_f = chunk_begin(cg, cf) < S ? 1 : 0;
-  auto rec_of = [&](int k) -> size_t {   // piece k of the segment
-    const int c = by_unit ? ((Si + k + 1) * W - 1) / Ti : cf + k;
+  auto rec_of = [&](int c, int k) -> size_t {   // piece k of the segment, in chunk c
     return (((size_t)c * 2 + (k == 0 ? slot_f : 0)) * NW + wv) * G + h;
   };
 
@@ -977,13 +980,20 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int i = 0; i < EPL; ++i) A[i] = 0.0f;
   for (int kb = wave; kb < np; kb += MW * UNROLL) {
-    // every load is issued (a piece past the last reads piece 0's record and is dropped)
+    // every load is issued (a piece past the last reads piece 0's record and is dropped).
+    // One unit per chunk: lane u works out the chunk of piece kb + u MW, so the round's
+    // divisions run side by side, and each load reads its chunk from that lane.
+    int cl = 0;
+    if (by_unit) {
+      const int kk = kb + (lane % UNROLL) * MW;
+      cl = ((Si + (kk < np ? kk : 0) + 1) * W - 1) / Ti;
+    }
     f32x2 mlp[UNROLL];
     float x[UNROLL][EPL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int k = kb + u * MW;
-      const size_t rec = rec_of(k < np ? k : 0);
+      const int k = kb + u * MW, kq = k < np ? k : 0;
+      const size_t rec = rec_of(by_unit ? __builtin_amdgcn_readlane(cl, u) : cf + kq, kq);
       mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
       load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
     }
@@ -1000,12 +1010,12 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
       M = Mn;
     }
   }
-  if (d0 == 0) {
+  if (dl == 0) {
     s_ml[wave][h][0] = M;
     s_ml[wave][h][1] = L;
   }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) s_acc[wave][h * D + d0 + e] = A[e];
+  for (int e = 0; e < EPL; ++e) s_acc[wave][h * DS + dl + e] = A[e];
   __syncthreads();
   if (wave != 0) return;
   float Mt = neg_inf();
@@ -1020,7 +1030,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
     const float f = mw == neg_inf() ? 0.0f : fast_exp2(mw - Mt);
     Lt = fmaf(s_ml[w][h][1], f, Lt);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) At[e] = fmaf(s_acc[w][h * D + d0 + e], f, At[e]);
+    for (int e = 0; e < EPL; ++e) At[e] = fmaf(s_acc[w][h * DS + dl + e], f, At[e]);
   }
   const float vsc = a.v_head_scales ? a.v_head_scales[g] : a.v_scale;
   const float inv = Lt > 0.0f ? vsc / Lt : 0.0f;
@@ -1093,13 +1103,19 @@ __global__ __launch_bounds__(kMaxThreads) void merge_chunk_kernel(MergeArgs a) {
     const int n = Ts > 0 ? Ts * c / W - u0 : c - cf;     // pieces before chunk c
     for (int kb = 0; kb < n; kb += UNROLL) {
       // every load is issued (a piece past the last reads chunk c's own record), so
-      // the UNROLL pieces cost one round trip; those past the last are dropped
+      // the UNROLL pieces cost one round trip; those past the last are dropped. One unit
+      // per chunk: lane u works out the chunk of piece kb + u (divisions side by side).
+      int cl = c;
+      if (Ts > 0) {
+        const int kk = kb + lane % UNROLL;
+        cl = kk >= n ? c : ((u0 + kk + 1) * W - 1) / Ts;
+      }
       f32x2 mlp[UNROLL];
       float x[UNROLL][EPL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int k = kb + u;
-        const int cc = k >= n ? c : Ts > 0 ? ((u0 + k + 1) * W - 1) / Ts : cf + k;
+        const int cc = Ts > 0 ? __builtin_amdgcn_readlane(cl, u) : (k >= n ? c : cf + k);
         const size_t rec = rec_of(cc, (k == 0) ? slot_f : 0);
         mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
         load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
@@ -1165,15 +1181,39 @@ hipError_t launch_merge_t(int group, const MergeArgs& args, hipStream_t stream) 
     }
     return hipGetLastError();
   }
-  // 4 waves fold 16 pieces per round trip; more waves only when a segment can have more
-  // pieces (most workgroups of a large batch exit at once, and launching idle waves costs)
-  const dim3 grid(args.num_kv_heads, args.batch);
-  auto waves = [&](int most) { return (args.max_pieces <= 16 ? 4 : most) * kWave; };
+  // 4 waves fold 16 or more pieces per round trip; more waves only when a segment can
+  // have more pieces (most workgroups of a large batch exit at once, and launching idle
+  // waves costs). Slices of the head dimension when there are few (kv head, sequence)
+  // pairs, up to 8 and while a lane keeps at least one output.
+  int S = 1;
+  while (S < 8 && (int64_t)args.num_kv_heads * args.batch * S < 512 && group * D >= 128 * S)
+    S *= 2;
+  const dim3 grid(args.num_kv_heads * S, args.batch);
+  auto launch = [&](auto g_tag, auto s_tag) {
+    constexpr int GG = decltype(g_tag)::value, SS = decltype(s_tag)::value;
+    if constexpr (GG * D >= 64 * SS) {
+      // enough waves for the pieces a segment typically has in one round trip, and at
+      // least 4, so that the folds of a few pieces run side by side
+      constexpr int EPL = GG * D / SS / kWave, UN = EPL >= 8 ? 4 : (EPL >= 4 ? 8 : 16);
+      const int need = (args.max_pieces + UN - 1) / UN;
+      int waves = 4;
+      while (waves < need && waves < merge_waves<GG, D, SS>()) waves *= 2;
+      merge_kernel<OT, D, GG, SS><<<grid, waves * kWave, 0, stream>>>(args);
+    }
+  };
+  auto by_slices = [&](auto g_tag) {
+    switch (S) {
+      case 1: launch(g_tag, std::integral_constant<int, 1>{}); break;
+      case 2: launch(g_tag, std::integral_constant<int, 2>{}); break;
+      case 4: launch(g_tag, std::integral_constant<int, 4>{}); break;
+      default: launch(g_tag, std::integral_constant<int, 8>{}); break;
+    }
+  };
   switch (group) {
-    case 1: merge_kernel<OT, D, 1><<<grid, waves(merge_waves<1, D>()), 0, stream>>>(args); break;
-    case 2: merge_kernel<OT, D, 2><<<grid, waves(merge_waves<2, D>()), 0, stream>>>(args); break;
-    case 4: merge_kernel<OT, D, 4><<<grid, waves(merge_waves<4, D>()), 0, stream>>>(args); break;
-    case 8: merge_kernel<OT, D, 8><<<grid, waves(merge_waves<8, D>()), 0, stream>>>(args); break;
+    case 1: by_slices(std::integral_constant<int, 1>{}); break;
+    case 2: by_slices(std::integral_constant<int, 2>{}); break;
+    case 4: by_slices(std::integral_constant<int, 4>{}); break;
+    case 8: by_slices(std::integral_constant<int, 8>{}); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

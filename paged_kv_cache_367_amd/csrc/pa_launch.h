@@ -111,7 +111,7 @@ struct MergeArgs {
   int32_t num_ranges;           // W0, decode workgroups
   int32_t part_units;
   int32_t chunk_merge;          // default split: 1 = merge_chunk_kernel, 0 = merge_kernel
-  int32_t max_pieces;           // most pieces a segment can be cut into (merge_kernel size)
+  int32_t max_pieces;           // pieces a segment typically has (sizes merge_kernel)
   float v_scale;
   const float* v_head_scales;   // [Hkv] or null
 };
