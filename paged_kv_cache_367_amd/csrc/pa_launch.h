@@ -63,9 +63,14 @@ __host__ __device__ inline int64_t chunk_begin(const ChunkGeom& g, int c) {
 __host__ __device__ inline int64_t chunk_end(const ChunkGeom& g, int c) {
   return static_bound(g, c + 1);
 }
-// chunk holding unit u (0 <= u < T): the last chunk starting at or before u
+// chunk holding unit u (0 <= u < T): the last chunk starting at or before u, i.e.
+// floor(((u + 1) W - 1) / T). In double precision, which is exact here and far shorter
+// than a 64-bit integer division on the GPU: the numerator is below 2^45 (u < 2^31,
+// W <= kMaxChunks) and the quotient below 2^14, so a quotient that is not an integer lies
+// at least 1/T, a relative 2^-45, below the next one, and rounding to 53 bits cannot
+// carry it there.
 __host__ __device__ inline int chunk_of(const ChunkGeom& g, int64_t u) {
-  return (int)(((u + 1) * g.W - 1) / g.T);
+  return (int)(((double)(u + 1) * (double)g.W - 1.0) / (double)g.T);
 }
 
 struct DecodeArgs {
