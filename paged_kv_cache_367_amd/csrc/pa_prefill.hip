@@ -15,12 +15,18 @@
 //   * K/V are staged through LDS 64 tokens (4 blocks) at a time, double-buffered: the
 //     global loads of the next tile are in flight while the current one is computed. fp8
 //     rows are widened to bf16 (exactly) on the way in, so the matrix cores see one
-//     layout. LDS rows are padded by 16 bytes to spread the banks.
+//     layout. K rows are padded by 16 bytes and V rows by 32 to spread the banks.
+//   * The P.V operand B (eight consecutive tokens of one output dim) comes straight from
+//     the row-major V tile through transposed LDS reads (ds_read_b64_tr_b16), so MFMA e
+//     covers output dims 16e + n; no byte permutes.
 //   * Scores run on the matrix cores as K.Q^T (v_mfma_f32_16x16x32_{bf16,f16}): lane
 //     (n, kq) = (lane % 16, lane / 16) ends with the scores of tokens 4kq .. 4kq+3 of each
 //     16-token subtile for row n, which is, two subtiles at a time, exactly the A-operand
 //     layout P takes in P.V, so P never leaves registers.
-//   * Online softmax per row (running max m and normaliser l, rescaled when m moves).
+//   * Online softmax per row (running max and normaliser l). The weights are taken
+//     against a reference max that moves only when the row's max outgrows it by more than
+//     2^8, so the accumulators are rescaled a few times per row instead of at most tiles
+//     (exact in real arithmetic: softmax does not depend on the reference).
 //     The matrix cores take p in 16 bits. fp16 (relative rounding 2^-11) is used as is,
 //     with l summing the rounded values so the output stays an exact weighted average of
 //     V rows. bf16 rounds p by up to 2^-9, which on rows that attend over a few tokens
@@ -49,9 +55,13 @@ namespace pa {
 namespace {
 
 constexpr int kTileTokens = 64;                      // K/V tokens per LDS tile
-#ifndef PA_PF_LPAD
-#define PA_PF_LPAD 16                                  // LDS row padding, bytes
-#endif
+// LDS row padding, bytes: K rows by 16 (the 16 rows a score operand read takes then sit
+// on distinct banks), V rows by 32 (the four rows a transposed read takes then do)
+constexpr int kKPad = 16, kVPad = 32;
+// Log2-domain growth of a row's max that moves its reference: below it, p = 2^(s - m_ref)
+// may reach 2^8, which fp32 sums and the 16-bit hi/lo parts of p carry without loss, and
+// the accumulators need no rescale.
+constexpr float kLazyMax = 8.0f;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kStageThreads = 256;                   // threads (4 whole waves) staging K/V
 
@@ -85,37 +95,14 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, float& ra, float& rb
   }
 }
 
-// N consecutive outputs from idx (16-byte aligned for 16-bit outputs of N = 8, 8-byte for
-// N = 4), converted to the output type.
-template <int OT, int N>
-__device__ __forceinline__ void store_run(void* out, size_t idx, const float (&x)[N]) {
-  if constexpr (OT == PA_F32) {
-    float* o = static_cast<float*>(out) + idx;
-#pragma unroll
-    for (int i = 0; i < N; i += 4)
-      *reinterpret_cast<f32x4*>(o + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
-  } else {
-    uint32_t w[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      float ra, rb;
-      w[i] = pack2<OT>(x[2 * i], x[2 * i + 1], ra, rb);
-    }
-    uint16_t* o = static_cast<uint16_t*>(out) + idx;
-    if constexpr (N == 8)
-      *reinterpret_cast<u32x4*>(o) = u32x4{w[0], w[1], w[2], w[3]};
-    else
-      *reinterpret_cast<u32x2*>(o) = u32x2{w[0], w[1]};
-  }
-}
-
 template <int KV, int OT, int D, int G, int RG>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int CT = KV == PA_F16 ? PA_F16 : PA_BF16;  // element type of the MFMAs
   constexpr bool SPLIT = KV == PA_BF16;                // p as hi + lo bf16 parts
   constexpr int KB = Enc<KV>::bytes;
   constexpr int ROWB = D * KB;                   // pool bytes of one token row, one kv head
-  constexpr int LROW = D * 2 + PA_PF_LPAD;       // LDS bytes of one token row (16-bit, padded)
+  constexpr int LROW = D * 2 + kKPad;            // LDS bytes of one K token row (16-bit)
+  constexpr int VROW = D * 2 + kVPad;            // LDS bytes of one V token row (16-bit)
   constexpr int ROWS = kPrefillWaves * RG * 16;  // (token, head) rows of the workgroup
   constexpr int TQ = ROWS / G;                   // query tokens of the workgroup
   constexpr int NC = D / 32;                     // 32-dim steps of a score MFMA chain
@@ -126,10 +113,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   using LT = typename VChunk<LB>::type;
   using LT2 = typename VChunk<(LB < 16 ? 2 * LB : 16)>::type;   // fp8 widened to bf16
   static_assert(ROWS % G == 0 && 16 % G == 0, "rows hold whole tokens");
-  using VW = typename std::conditional<DPL == 8, u32x4, u32x2>::type;  // DPL 16-bit values
 
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kTileTokens * LROW];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kTileTokens * LROW];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kTileTokens * VROW];
 
   // ---- which (sequence, kv head, query tile): id = ((group * tiles) + tile') * 8 + x,
   // pair = group * 8 + x, tile = tiles - 1 - tile'
@@ -247,7 +233,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = kBlockTokens * i + tid / TPR;
-      const int at = tok * LROW + (tid % TPR) * LB * (KV == PA_FP8_E4M3 ? 2 : 1);
+      const int col = (tid % TPR) * LB * (KV == PA_FP8_E4M3 ? 2 : 1);
+      const int at = tok * LROW + col, atv = tok * VROW + col;
       if constexpr (KV == PA_FP8_E4M3) {
         // LB E4M3 values -> LB bf16 (exact)
         constexpr int W = LB / 4;
@@ -270,16 +257,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           vx[w] = vw[w];
         }
         *reinterpret_cast<LT2*>(&s_k[buf][at]) = kx;
-        *reinterpret_cast<LT2*>(&s_v[buf][at]) = vx;
+        *reinterpret_cast<LT2*>(&s_v[buf][atv]) = vx;
       } else {
         *reinterpret_cast<LT*>(&s_k[buf][at]) = kr[i];
-        *reinterpret_cast<LT*>(&s_v[buf][at]) = vr[i];
+        *reinterpret_cast<LT*>(&s_v[buf][atv]) = vr[i];
       }
     }
   };
 
-  // ---- running state: row li's max m (log2 units) and partial normaliser l (this lane's
-  // tokens), and acc[rg][e]: lane (j, g) holds rows 4g + v, dim DPL*j + e
+  // ---- running state: row li's reference max m (log2 units; the running max, moved only
+  // when the max outgrows it by more than kLazyMax), partial normaliser l (this lane's
+  // tokens) and acc[rg][e]: lane (j, g) holds rows 4g + v, dim 16e + j
   float m[RG], l[RG];
   f32x4 acc[RG][DPL];
 #pragma unroll
@@ -325,7 +313,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           live[s][v] = !MASKED || kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg];
           bm = fmaxf(bm, live[s][v] ? sc[rg][s][v] : neg_inf());
         }
-      const float mn = xrow_max(fmaxf(bm * qks, m[rg]));
+      const float mx = xrow_max(fmaxf(bm * qks, m[rg]));   // the row's running max
+      const float mn = mx > m[rg] + kLazyMax ? mx : m[rg];  // its reference (-inf at first)
       const float base = mn == neg_inf() ? 0.0f : mn;
       // p = 2^(s * scale - max); masked positions are 0 (also for a zero scale)
       float sv[4][4];
@@ -377,23 +366,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           for (int v = 0; v < 4; ++v) acc[rg][e][v] *= alv[v];
       }
     }
-    // P.V: k-slot 8lk + e is token 32pi + 4lk + e (e < 4) or 32pi + 16 + 4lk + e - 4
+    // P.V: k-slot 8lk + i is token 32pi + 4lk + i (i < 4) or 32pi + 16 + 4lk + i - 4, and
+    // MFMA e covers output dims 16e + n (column n). Its B operand, dim 16e + n of those
+    // eight tokens, comes from two transposed LDS reads (ds_read_b64_tr_b16): in each
+    // 16-lane group lane i receives element i % 4 of the 8-byte rows that lanes i / 4,
+    // i / 4 + 4, i / 4 + 8 and i / 4 + 12 point at, so lane R points at token t0 + R / 4,
+    // dims 16e + 4 (R % 4) .. + 3, and lane n gets dim 16e + n of tokens t0 .. t0 + 3.
+    const int tq = li >> 2, dq = 4 * (li & 3);
 #pragma unroll
     for (int pi = 0; pi < 2; ++pi) {
-      VW vr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = 32 * pi + (e < 4 ? 4 * lk + e : 16 + 4 * lk + e - 4);
-        vr[e] = *reinterpret_cast<const VW*>(Vt + tok * LROW + li * DPL * 2);
-      }
+      const uint8_t* vrow = Vt + (32 * pi + 4 * lk + tq) * VROW + dq * 2;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int w = e >> 1;
-        const u32x4 bop = {__builtin_amdgcn_perm(vr[1][w], vr[0][w], sel),
-                           __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel),
-                           __builtin_amdgcn_perm(vr[5][w], vr[4][w], sel),
-                           __builtin_amdgcn_perm(vr[7][w], vr[6][w], sel)};
+        const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vrow + 32 * e));
+        const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vrow + 16 * VROW + 32 * e));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, b0), w1 = __builtin_bit_cast(u32x2, b1);
+        const u32x4 bop = {w0[0], w0[1], w1[0], w1[1]};
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           acc[rg][e] = mfma32<CT>(aop[rg][pi], bop, acc[rg][e]);
@@ -434,7 +424,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   for (; kt < nfree; ++kt) step(kt, std::false_type{});
   for (; kt < ntiles; ++kt) step(kt, std::true_type{});
 
-  // ---- normalise and store: lane (j, lk) writes rows 4lk + v, dims DPL*j .. DPL*j+DPL-1
+  // ---- normalise and store: lane (j, lk) writes rows 4lk + v, dims 16e + j
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const float lt = xrow_sum(l[rg]);
@@ -445,10 +435,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       const int t = t0 + r / G, h = r % G;
       if (t >= nr) continue;
       const float inv = lr > 0.0f ? vsc / lr : 0.0f;
-      float o[DPL];
+      const size_t o = ((size_t)(qs0 + t) * Hq + (size_t)kvh * G + h) * D + li;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = acc[rg][e][v] * inv;
-      store_run<OT, DPL>(a.out, ((size_t)(qs0 + t) * Hq + (size_t)kvh * G + h) * D + DPL * li, o);
+      for (int e = 0; e < DPL; ++e) store_out<OT>(a.out, o + 16 * e, acc[rg][e][v] * inv);
     }
   }
 }
