@@ -64,28 +64,32 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_367_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_device.h")]
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.md")
+PREFILL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_367_amd", "csrc", f)
+                   for f in ("pa_prefill.hip", "pa_device.h")]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the decode kernel's sources, concatenated."""
+def kernel_source_hash(sources=None) -> str:
+    """sha256 (first 16 hex digits) of a kernel's sources (default: the decode's),
+    concatenated."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(config_name: str):
-    """HBM bytes per decode launch from the committed counter summary, or None when the
-    summary is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(config_name: str, path: str = TRAFFIC_FILE, sources=None):
+    """HBM bytes per launch from a committed counter summary, or None when the summary is
+    missing or was taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not h or h.group(1) != kernel_source_hash():
+    if not h or h.group(1) != kernel_source_hash(sources):
         return None
     m = re.search(rf"traffic_bytes_per_launch\[{re.escape(config_name)}\]:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
@@ -300,7 +304,9 @@ def run_prefill(args) -> int:
         "roofline": {
             "kernel": "pa_prefill (prefill_kernel)", "bound": "mfma", "achieved": achieved,
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "launch_ms": lavg,
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": read_traffic(w.name, PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
+            "launch_ms": lavg,
             "algorithmic_flops_per_launch": flops,
         },
         "cpu_baseline": None,
