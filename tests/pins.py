@@ -273,6 +273,38 @@ def pin_brute_force_scalar():
         assert np.max(np.abs(ref - bf)) <= 1e-12, w.name
 
 
+def pin_block_removed_from_table():
+    """Dropping a full block from a sequence's table (and 16 from its length) gives the
+    attention over the sequence's other tokens, by brute force: the expected value the GPU
+    tests use for a block id outside the pool, whose tokens the kernels leave out."""
+    import dataclasses
+    tabs = _torch_tables()
+    w = _small(kv="bf16", G=2, Hkv=1, d=64, lens=(40, 33))
+    j = 1                                               # the middle block of sequence 0
+    t2 = w.block_tables.copy()
+    t2[0, :2] = [w.block_tables[0, 0], w.block_tables[0, 2]]
+    t2[0, 2] = -1
+    red = dataclasses.replace(w, block_tables=t2,
+                              context_lens=np.array([24, 33], dtype=np.int32))
+    got = _ref(red)
+    # brute force over the original table, skipping tokens 16 .. 31 of sequence 0
+    keep = [t for t in range(40) if t // 16 != j]
+    qb = _decode_lib(w.q[0], w.q_dtype, tabs).tolist()
+    for h in range(w.num_q_heads):
+        ks = [_decode_lib(w.k_pool[w.block_tables[0][t // 16]][t % 16][0], w.kv_dtype,
+                          tabs).tolist() for t in keep]
+        vs = [_decode_lib(w.v_pool[w.block_tables[0][t // 16]][t % 16][0], w.kv_dtype,
+                          tabs).tolist() for t in keep]
+        s = [w.scale * math.fsum(qb[h][i] * k[i] for i in range(w.head_dim)) for k in ks]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        z = math.fsum(e)
+        want = [math.fsum(e[t] * vs[t][i] for t in range(len(keep))) / z
+                for i in range(w.head_dim)]
+        assert np.max(np.abs(got[0, h] - np.array(want))) <= 1e-12
+    assert np.array_equal(got[1], _ref(w)[1])          # the other sequence is untouched
+
+
 def pin_sdpa_library():
     """torch's scaled_dot_product_attention in float64 on the contiguous cache."""
     import torch
