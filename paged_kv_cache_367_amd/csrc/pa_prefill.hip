@@ -13,9 +13,10 @@
 //     rows are (token, head) pairs, row r = token r / G, head r % G, so the G query heads
 //     that share a kv head share every K/V byte: each wave owns RG groups of 16 rows.
 //   * K/V are staged through LDS 64 tokens (4 blocks) at a time, double-buffered: the
-//     global loads of the next tile are in flight while the current one is computed. fp8
-//     rows are widened to bf16 (exactly) on the way in, so the matrix cores see one
-//     layout. K rows are padded by 16 bytes and V rows by 32 to spread the banks.
+//     global loads of the next tile are in flight while the current one is computed. K
+//     rows reach LDS in the score type (bf16 for bf16 and fp8 K, fp16 for fp16; fp8
+//     widened exactly), V rows in fp16 (fp8 widened exactly, bf16 converted: see below).
+//     K rows are padded by 16 bytes and V rows by 32 to spread the banks.
 //   * The P.V operand B (eight consecutive tokens of one output dim) comes straight from
 //     the row-major V tile through transposed LDS reads (ds_read_b64_tr_b16), so MFMA e
 //     covers output dims 16e + n; no byte permutes.
@@ -27,17 +28,21 @@
 //     against a reference max that moves only when the row's max outgrows it by more than
 //     2^8, so the accumulators are rescaled a few times per row instead of at most tiles
 //     (exact in real arithmetic: softmax does not depend on the reference).
-//     The matrix cores take p in 16 bits. fp16 (relative rounding 2^-11) is used as is,
-//     with l summing the rounded values so the output stays an exact weighted average of
-//     V rows. bf16 rounds p by up to 2^-9, which on rows that attend over a few tokens
-//     moves the output by a visible fraction of the spread of V; for bf16 K/V p is
-//     therefore split into hi (p with its low 16 bits cleared, exact) and lo = bf16(p -
-//     hi), and P.V takes both (weights exact to about 2^-16, at twice the P.V matrix
-//     work; l sums p itself). fp8 K/V, whose own rounding is far coarser, takes the
-//     single bf16 pass.
+//     P.V runs on the matrix cores in fp16 for every K/V type: p rounded to fp16
+//     (relative rounding 2^-11) against fp16 V, with the normaliser taken by the same
+//     MFMAs (P times a column of ones), so that it sums exactly the rounded weights and
+//     the output stays an exact weighted average of V rows. bf16 V converts to fp16
+//     exactly below 2^16 in magnitude (values under 2^-17 move by less than 2^-25). Where
+//     a workgroup meets a bf16 V value of 2^16 or more (or an infinity or NaN) it runs its
+//     key loop again with V staged as bf16 and p split into hi (p with its low 16 bits
+//     cleared, exact) and lo = bf16(p - hi), both taken by bf16 MFMAs (weights exact to
+//     about 2^-16, at twice the P.V matrix work). bf16 weights in one pass (rounding up
+//     to 2^-9) would move the output of rows attending over a few tokens by a visible
+//     fraction of the spread of V.
 //   * Tiles wholly at or before the tile's first query position need no mask; the rest
 //     mask positions past each row's own. A block id outside the pool is never read; its
-//     16 tokens get a score of -inf (weight 0) in every row.
+//     16 tokens get weight 0 in every row (from the first tile holding one, every tile
+//     takes the masked body).
 //   * Workgroup ids are dealt so that all query tiles of one (sequence, kv head) land on
 //     the same XCD (workgroups go to the 8 XCDs round-robin) and share its L2; within a
 //     pair, later tiles (longer key ranges) start first.
@@ -76,29 +81,19 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 acc) {
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
-// Two floats rounded to CT (nearest even) and packed, a in the low half; ra, rb get the
-// rounded values.
-template <int CT>
-__device__ __forceinline__ uint32_t pack2(float a, float b, float& ra, float& rb) {
-  if constexpr (CT == PA_F16) {
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    ra = (float)ha;
-    rb = (float)hb;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           (uint32_t)__builtin_bit_cast(uint16_t, hb) << 16;
-  } else {
-    const bf16x2 h = {(__bf16)a, (__bf16)b};
-    const uint32_t w = __builtin_bit_cast(uint32_t, h);
-    ra = __uint_as_float(w << 16);
-    rb = __uint_as_float(w & 0xffff0000u);
-    return w;
-  }
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to fp16 / bf16 (nearest even) and packed, a in the low half.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 template <int KV, int OT, int D, int G, int RG>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
-  constexpr int CT = KV == PA_F16 ? PA_F16 : PA_BF16;  // element type of the MFMAs
-  constexpr bool SPLIT = KV == PA_BF16;                // p as hi + lo bf16 parts
+  constexpr int ST = KV == PA_F16 ? PA_F16 : PA_BF16;  // element type of the score MFMAs
   constexpr int KB = Enc<KV>::bytes;
   constexpr int ROWB = D * KB;                   // pool bytes of one token row, one kv head
   constexpr int LROW = D * 2 + kKPad;            // LDS bytes of one K token row (16-bit)
@@ -228,7 +223,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       vr[i] = VChunk<LB>::load(make_rsrc(vpool + base, bytes), ld_off);
     }
   };
-  auto to_lds = [&](int buf, const LT (&kr)[4], const LT (&vr)[4]) {
+  // V rows go to LDS as fp16 for the P.V matrix cores: fp16 and fp8 (exactly widened) as
+  // they are, bf16 converted (exact for every |v| below 2^16, the tiniest values aside,
+  // which move by less than 2^-25). vmax tracks the largest |v| converted; a bf16 V
+  // value of 2^16 or more, an infinity or a NaN sends the workgroup through the pass again
+  // with V staged as bf16 and p split into two bf16 parts (FB).
+  float vmax = 0.0f;
+  auto to_lds = [&](int buf, const LT (&kr)[4], const LT (&vr)[4], auto fb_tag) {
+    constexpr bool FB = decltype(fb_tag)::value;
     if (!stager) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -236,50 +238,55 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       const int col = (tid % TPR) * LB * (KV == PA_FP8_E4M3 ? 2 : 1);
       const int at = tok * LROW + col, atv = tok * VROW + col;
       if constexpr (KV == PA_FP8_E4M3) {
-        // LB E4M3 values -> LB bf16 (exact)
+        // LB E4M3 values -> LB bf16 (K) and LB fp16 (V), both exact
         constexpr int W = LB / 4;
-        uint32_t kw[2 * W], vw[2 * W];
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          kw[2 * w] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, false));
-          kw[2 * w + 1] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, true));
-          vw[2 * w] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, false));
-          vw[2 * w + 1] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[i][w], 1.0f, true));
-        }
         LT2 kx, vx;
 #pragma unroll
-        for (int w = 0; w < 2 * W; ++w) {
-          kx[w] = kw[w];
-          vx[w] = vw[w];
+        for (int w = 0; w < W; ++w) {
+          kx[2 * w] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, false));
+          kx[2 * w + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, true));
+          vx[2 * w] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[i][w], 1.0f, false));
+          vx[2 * w + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[i][w], 1.0f, true));
         }
         *reinterpret_cast<LT2*>(&s_k[buf][at]) = kx;
         *reinterpret_cast<LT2*>(&s_v[buf][atv]) = vx;
       } else {
         *reinterpret_cast<LT*>(&s_k[buf][at]) = kr[i];
-        *reinterpret_cast<LT*>(&s_v[buf][atv]) = vr[i];
+        if constexpr (KV == PA_BF16 && !FB) {
+          LT vx;
+#pragma unroll
+          for (int w = 0; w < LB / 4; ++w) {
+            const float lo = __uint_as_float(vr[i][w] << 16);
+            const float hi = __uint_as_float(vr[i][w] & 0xffff0000u);
+            vmax = __builtin_elementwise_maximum(            // NaN-propagating
+                vmax, __builtin_elementwise_maximum(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+            vx[w] = pack_f16(lo, hi);
+          }
+          *reinterpret_cast<LT*>(&s_v[buf][atv]) = vx;
+        } else {
+          *reinterpret_cast<LT*>(&s_v[buf][atv]) = vr[i];
+        }
       }
     }
   };
 
   // ---- running state: row li's reference max m (log2 units; the running max, moved only
-  // when the max outgrows it by more than kLazyMax), partial normaliser l (this lane's
-  // tokens) and acc[rg][e]: lane (j, g) holds rows 4g + v, dim 16e + j
-  float m[RG], l[RG];
-  f32x4 acc[RG][DPL];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    m[rg] = neg_inf();
-    l[rg] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[rg][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  // when the max outgrows it by more than kLazyMax); acc[rg][e]: lane (j, g) holds rows
+  // 4g + v, dim 16e + j; lsum[rg]: lane (j, g) holds the normaliser of rows 4g + v (P
+  // times a column of ones on the matrix cores: the sum of exactly the weights P.V takes)
+  float m[RG];
+  f32x4 acc[RG][DPL], lsum[RG];
 
-  auto compute = [&](int buf, int kt, int bad, auto masked_tag) {
+  // one key tile: scores, online softmax, P.V. MASKED: positions past a row's own, and the
+  // blocks flagged in `bad`, get weight 0. FB: V staged as bf16, p as hi + lo bf16 parts.
+  auto compute = [&](int buf, int kt, int bad, auto masked_tag, auto fb_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool FB = decltype(fb_tag)::value;
+    constexpr int PT = FB ? PA_BF16 : PA_F16;           // element type of the P.V MFMAs
     const uint8_t* Kt = s_k[buf];
     const uint8_t* Vt = s_v[buf];
     // scores: sc[rg][s][v] = row li of group rg against token 16s + 4lk + v
@@ -294,13 +301,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       for (int rg = 0; rg < RG; ++rg) {
         f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) z = mfma32<CT>(kop[c], qop[rg][c], z);
+        for (int c = 0; c < NC; ++c) z = mfma32<ST>(kop[c], qop[rg][c], z);
         sc[rg][s] = z;
-        if (bad & (1 << s)) sc[rg][s] = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
       }
     }
     u32x4 aop[RG][2];                      // P as the A operand, two subtiles per MFMA
-    u32x4 alo[SPLIT ? RG : 1][2];          // the low parts of P (bf16 K/V)
+    u32x4 alo[FB ? RG : 1][2];             // the low parts of P (FB)
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       // raw scores; the max commutes with the (non-negative) scale, rounding included
@@ -310,7 +316,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          live[s][v] = !MASKED || kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg];
+          live[s][v] = !MASKED || (kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] &&
+                                   !((bad >> s) & 1));
           bm = fmaxf(bm, live[s][v] ? sc[rg][s][v] : neg_inf());
         }
       const float mx = xrow_max(fmaxf(bm * qks, m[rg]));   // the row's running max
@@ -323,7 +330,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) sv[s][v] = fmaf(sc[rg][s][v], qks, -base);
       const float al = m[rg] == mn ? 1.0f : fast_exp2(m[rg] - base);
-      float ls = 0.0f;
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi) {
         uint32_t w[4], wl[4];
@@ -337,33 +343,30 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
               pa = live[2 * pi + h][v] ? pa : 0.0f;
               pb = live[2 * pi + h][v + 1] ? pb : 0.0f;
             }
-            if constexpr (SPLIT) {
+            if constexpr (FB) {
               const uint32_t ua = __float_as_uint(pa), ub = __float_as_uint(pb);
               w[2 * h + v / 2] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // high halves
-              float la, lb;
-              wl[2 * h + v / 2] = pack2<CT>(pa - __uint_as_float(ua & 0xffff0000u),
-                                            pb - __uint_as_float(ub & 0xffff0000u), la, lb);
-              ls += pa + pb;
+              wl[2 * h + v / 2] = pack_bf16(pa - __uint_as_float(ua & 0xffff0000u),
+                                            pb - __uint_as_float(ub & 0xffff0000u));
             } else {
-              float ra, rb;
-              w[2 * h + v / 2] = pack2<CT>(pa, pb, ra, rb);
-              ls += ra + rb;
+              w[2 * h + v / 2] = pack_f16(pa, pb);
             }
           }
         aop[rg][pi] = u32x4{w[0], w[1], w[2], w[3]};
-        if constexpr (SPLIT) alo[rg][pi] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+        if constexpr (FB) alo[rg][pi] = u32x4{wl[0], wl[1], wl[2], wl[3]};
       }
-      l[rg] = l[rg] * al + ls;
       m[rg] = mn;
-      // rows 4lk + v of the accumulator take the factor of row 4lk + v (held by lane 4lk + v)
+      // rows 4lk + v of the accumulators take the factor of row 4lk + v (held by lane 4lk + v)
       if (__builtin_amdgcn_ballot_w64(al != 1.0f) != 0) {
         float alv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) alv[v] = __shfl(al, 4 * lk + v);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e)
+        for (int v = 0; v < 4; ++v) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[rg][e][v] *= alv[v];
+          for (int e = 0; e < DPL; ++e) acc[rg][e][v] *= alv[v];
+          lsum[rg][v] *= alv[v];
+        }
       }
     }
     // P.V: k-slot 8lk + i is token 32pi + 4lk + i (i < 4) or 32pi + 16 + 4lk + i - 4, and
@@ -372,9 +375,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     // 16-lane group lane i receives element i % 4 of the 8-byte rows that lanes i / 4,
     // i / 4 + 4, i / 4 + 8 and i / 4 + 12 point at, so lane R points at token t0 + R / 4,
     // dims 16e + 4 (R % 4) .. + 3, and lane n gets dim 16e + n of tokens t0 .. t0 + 3.
+    // A B operand of ones (1.0 in PT) adds each row's weights to lsum.
+    const uint32_t one2 = PT == PA_F16 ? 0x3c003c00u : 0x3f803f80u;
+    const u32x4 ones = {one2, one2, one2, one2};
     const int tq = li >> 2, dq = 4 * (li & 3);
 #pragma unroll
     for (int pi = 0; pi < 2; ++pi) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        lsum[rg] = mfma32<PT>(aop[rg][pi], ones, lsum[rg]);
+        if constexpr (FB) lsum[rg] = mfma32<PT>(alo[rg][pi], ones, lsum[rg]);
+      }
       const uint8_t* vrow = Vt + (32 * pi + 4 * lk + tq) * VROW + dq * 2;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
@@ -386,51 +397,65 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         const u32x4 bop = {w0[0], w0[1], w1[0], w1[1]};
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-          acc[rg][e] = mfma32<CT>(aop[rg][pi], bop, acc[rg][e]);
-          if constexpr (SPLIT) acc[rg][e] = mfma32<CT>(alo[rg][pi], bop, acc[rg][e]);
+          acc[rg][e] = mfma32<PT>(aop[rg][pi], bop, acc[rg][e]);
+          if constexpr (FB) acc[rg][e] = mfma32<PT>(alo[rg][pi], bop, acc[rg][e]);
         }
       }
     }
   };
 
-  // ---- the key loop: stage tile kt + 1 (ids one tile further ahead) while computing kt
-  u32x4 idv = {0u, 0u, 0u, 0u};
-  LT kr[4], vr[4];
-  int bad_next = 0;                        // bad blocks of the tile staged last
-  if (ntiles > 0) {
-    idv = load_ids(0);
-    bad_next = bad_blocks(0, idv);
-    stage(0, idv, kr, vr);
-    idv = load_ids(1);
-    to_lds(0, kr, vr);
-  }
-  __syncthreads();
-  auto step = [&](int kt, auto masked_tag) {
-    const bool more = kt + 1 < ntiles;
-    const int bad = bad_next;
-    if (more) {
-      bad_next = bad_blocks(kt + 1, idv);
-      stage(kt + 1, idv, kr, vr);
-      idv = load_ids(kt + 2);
+  // ---- the key loop: stage tile kt + 1 (ids one tile further ahead) while computing kt.
+  // Tiles wholly at or before the first query position need no mask, unless a block of
+  // theirs lies outside the pool; from the first tile that needs one on, all take the
+  // masked body. Two loops, so that each body is compiled (and its registers allocated)
+  // on its own.
+  auto run = [&](auto fb_tag) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      m[rg] = neg_inf();
+      lsum[rg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[rg][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    compute(kt & 1, kt, bad, masked_tag);
-    if (more) to_lds((kt + 1) & 1, kr, vr);
+    u32x4 idv = {0u, 0u, 0u, 0u};
+    LT kr[4], vr[4];
+    int bad_next = 0;                      // bad blocks of the tile staged last
+    if (ntiles > 0) {
+      idv = load_ids(0);
+      bad_next = bad_blocks(0, idv);
+      stage(0, idv, kr, vr);
+      idv = load_ids(1);
+      to_lds(0, kr, vr, fb_tag);
+    }
     __syncthreads();
+    auto step = [&](int kt, auto masked_tag) {
+      const bool more = kt + 1 < ntiles;
+      const int bad = bad_next;
+      if (more) {
+        bad_next = bad_blocks(kt + 1, idv);
+        stage(kt + 1, idv, kr, vr);
+        idv = load_ids(kt + 2);
+      }
+      compute(kt & 1, kt, bad, masked_tag, fb_tag);
+      if (more) to_lds((kt + 1) & 1, kr, vr, fb_tag);
+      __syncthreads();
+    };
+    const int nfree = nfull < ntiles ? nfull : ntiles;
+    int kt = 0;
+    for (; kt < nfree && bad_next == 0; ++kt) step(kt, std::false_type{});
+    for (; kt < ntiles; ++kt) step(kt, std::true_type{});
   };
-  // tiles wholly at or before the first query position, then the masked rest: two loops,
-  // so that each body is compiled (and its registers allocated) on its own
-  const int nfree = nfull < ntiles ? nfull : ntiles;
-  int kt = 0;
-  for (; kt < nfree; ++kt) step(kt, std::false_type{});
-  for (; kt < ntiles; ++kt) step(kt, std::true_type{});
+  run(std::false_type{});
+  if constexpr (KV == PA_BF16) {
+    if (__syncthreads_or(!(vmax < 65536.0f))) run(std::true_type{});
+  }
 
   // ---- normalise and store: lane (j, lk) writes rows 4lk + v, dims 16e + j
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const float lt = xrow_sum(l[rg]);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float lr = __shfl(lt, 4 * lk + v);
+      const float lr = lsum[rg][v];
       const int r = (wave * RG + rg) * 16 + 4 * lk + v;
       const int t = t0 + r / G, h = r % G;
       if (t >= nr) continue;
