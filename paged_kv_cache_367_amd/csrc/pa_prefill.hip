@@ -68,7 +68,6 @@ constexpr int kKPad = 16, kVPad = 32;
 // the accumulators need no rescale.
 constexpr float kLazyMax = 8.0f;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
-constexpr int kStageThreads = 256;                   // threads (4 whole waves) staging K/V
 
 // One 16x16x32 MFMA in the 16-bit type CT: acc += A * B.
 template <int CT>
@@ -102,11 +101,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr int TQ = ROWS / G;                   // query tokens of the workgroup
   constexpr int NC = D / 32;                     // 32-dim steps of a score MFMA chain
   constexpr int DPL = D / 16;                    // output dims per lane and 16-row group
-  constexpr int LB = kBlockTokens * ROWB / kStageThreads;  // staged bytes per thread and block
-  constexpr int TPR = ROWB / LB;                 // threads per token row
-  static_assert(LB == 16 || LB == 8 || LB == 4, "one load per thread and block");
-  using LT = typename VChunk<LB>::type;
-  using LT2 = typename VChunk<(LB < 16 ? 2 * LB : 16)>::type;   // fp8 widened to bf16
   static_assert(ROWS % G == 0 && 16 % G == 0, "rows hold whole tokens");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kTileTokens * LROW];
@@ -181,97 +175,104 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qop[rg][c]));
 
-  // ---- K/V staging. One load instruction per 16-token block: thread tid moves LB bytes
-  // (16, 8 or 4) at token tid / TPR, byte tid % TPR * LB of the kv head's row, through a
-  // per-block scalar descriptor whose size stops at position L, so later rows read as
-  // zero (stale or NaN slots never meet a p = 0) and missing blocks cost nothing
+  // ---- K/V staging. Wave w stages block 4kt + w of tile kt: lane l moves NLD 16-byte
+  // pieces, piece j holding row j * RPL + l / TPC at bytes (l % TPC) * 16 .. + 15 of the
+  // kv head's row (TPC lanes per row), through one scalar descriptor per block whose size
+  // stops at position L, so later rows read as zero (stale or NaN slots never meet a
+  // p = 0) and a missing block costs nothing.
+  static_assert(kPrefillWaves == 4, "one wave per block of a 64-token tile");
+  constexpr int TPC = ROWB / 16;                 // lanes per token row
+  constexpr int RPL = kWave / TPC;               // token rows per load instruction
+  constexpr int NLD = kBlockTokens / RPL;        // loads per lane, block and pool
+  static_assert(TPC * 16 == ROWB && RPL * TPC == kWave && NLD * RPL == kBlockTokens,
+                "whole rows per load");
   const uint32_t tok_stride = (uint32_t)a.num_kv_heads * ROWB;
   const size_t blk_stride = (size_t)kBlockTokens * tok_stride;
   const uint8_t* const kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)kvh * ROWB;
   const uint8_t* const vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)kvh * ROWB;
-  const uint32_t ld_off = (uint32_t)(tid / TPR) * tok_stride + (uint32_t)(tid % TPR) * LB;
-  // block ids of a tile's 4 blocks: one 16-byte load (table entries j = 4kt .. 4kt+3, the
-  // same for every lane) issued with the K/V prefetch of the tile before, so its wait is
-  // the one the K/V data already takes; entries at or past nb read as 0 and are never used
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j)
+    ld_off[j] = (uint32_t)(j * RPL + lane / TPC) * tok_stride + (uint32_t)(lane % TPC) * 16u;
+  // the block id of wave w's block in tile kt (table entry 4kt + w, the same for every lane
+  // of the wave), loaded one tile ahead with the K/V prefetch of the tile before, so its
+  // wait is the one the K/V data already takes; entries at or past nb read as 0 and are
+  // never used
   const __amdgpu_buffer_rsrc_t rt =
       make_rsrc(a.block_tables + (size_t)b * a.max_blocks_per_seq, (uint32_t)nb * 4u);
-  auto load_ids = [&](int kt) -> u32x4 { return buf_load16(rt, (uint32_t)kt * 16u); };
-  const bool stager = kPrefillThreads == kStageThreads || wave < kStageThreads / kWave;
-  // blocks of tile kt below L whose id lies outside the pool (bit i: block 4kt + i): they
-  // are never read, and their 16 tokens are masked out of the softmax
-  auto bad_blocks = [&](int kt, const u32x4& idv) -> int {
-    int bad = 0;
+  auto load_id = [&](int kt) -> uint32_t { return buf_load4(rt, (uint32_t)(kt * 4 + wave) * 4u); };
+  // K/V of wave w's block in tile kt into registers; returns whether the block lies below
+  // L with an id outside the pool (never read; its 16 tokens are masked out of the softmax)
+  auto stage = [&](int kt, uint32_t id, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) -> bool {
+    const int rem = L - (kt * 4 + wave) * kBlockTokens;   // rows of the block below L
+    const uint32_t pid = (uint32_t)uni((int)id);
+    const bool ok = rem > 0 && pid < (uint32_t)a.num_blocks;
+    // (selects, not branches: the scalar unit computes both sides)
+    const size_t base = (size_t)(ok ? pid : 0u) * blk_stride;
+    const uint32_t rows = (uint32_t)(rem < kBlockTokens ? rem : kBlockTokens);
+    const uint32_t bytes = ok ? (rows - 1u) * tok_stride + ROWB : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rem = L - (kt * 4 + i) * kBlockTokens;
-      bad |= (rem > 0 && (uint32_t)uni((int)idv[i]) >= (uint32_t)a.num_blocks) ? 1 << i : 0;
+    for (int j = 0; j < NLD; ++j) {
+      kr[j] = buf_load16(rk, ld_off[j]);
+      vr[j] = buf_load16(rv, ld_off[j]);
     }
-    return uni(bad);
+    return rem > 0 && !ok;
   };
-  auto stage = [&](int kt, const u32x4& idv, LT (&kr)[4], LT (&vr)[4]) {
-    if (!stager) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = kt * 4 + i;
-      const int rem = L - j * kBlockTokens;             // rows of the block below L
-      const uint32_t pid = (uint32_t)uni((int)idv[i]);
-      const bool ok = rem > 0 && pid < (uint32_t)a.num_blocks;
-      const size_t base = ok ? (size_t)pid * blk_stride : 0;
-      const uint32_t bytes =
-          ok ? (uint32_t)((rem < kBlockTokens ? rem : kBlockTokens) - 1) * tok_stride + ROWB : 0u;
-      kr[i] = VChunk<LB>::load(make_rsrc(kpool + base, bytes), ld_off);
-      vr[i] = VChunk<LB>::load(make_rsrc(vpool + base, bytes), ld_off);
-    }
-  };
+  // per LDS buffer, one byte per wave: its block of the tile staged there is out of pool
+  __shared__ uint32_t s_bad[2];
   // V rows go to LDS as fp16 for the P.V matrix cores: fp16 and fp8 (exactly widened) as
   // they are, bf16 converted (exact for every |v| below 2^16, the tiniest values aside,
   // which move by less than 2^-25). vmax tracks the largest |v| converted; a bf16 V
   // value of 2^16 or more, an infinity or a NaN sends the workgroup through the pass again
   // with V staged as bf16 and p split into two bf16 parts (FB).
   float vmax = 0.0f;
-  auto to_lds = [&](int buf, const LT (&kr)[4], const LT (&vr)[4], auto fb_tag) {
+  auto to_lds = [&](int buf, const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD], bool bad,
+                    auto fb_tag) {
     constexpr bool FB = decltype(fb_tag)::value;
-    if (!stager) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = kBlockTokens * i + tid / TPR;
-      const int col = (tid % TPR) * LB * (KV == PA_FP8_E4M3 ? 2 : 1);
+    for (int j = 0; j < NLD; ++j) {
+      const int tok = kBlockTokens * wave + j * RPL + lane / TPC;
+      const int col = (lane % TPC) * 16 * (KV == PA_FP8_E4M3 ? 2 : 1);
       const int at = tok * LROW + col, atv = tok * VROW + col;
       if constexpr (KV == PA_FP8_E4M3) {
-        // LB E4M3 values -> LB bf16 (K) and LB fp16 (V), both exact
-        constexpr int W = LB / 4;
-        LT2 kx, vx;
+        // 16 E4M3 values -> 16 bf16 (K) and 16 fp16 (V), both exact
+        u32x4 kx[2], vx[2];
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-          kx[2 * w] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, false));
-          kx[2 * w + 1] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[i][w], 1.0f, true));
-          vx[2 * w] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[i][w], 1.0f, false));
-          vx[2 * w + 1] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[i][w], 1.0f, true));
+        for (int w = 0; w < 4; ++w) {
+          kx[w / 2][2 * (w % 2)] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[j][w], 1.0f, false));
+          kx[w / 2][2 * (w % 2) + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[j][w], 1.0f, true));
+          vx[w / 2][2 * (w % 2)] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[j][w], 1.0f, false));
+          vx[w / 2][2 * (w % 2) + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vr[j][w], 1.0f, true));
         }
-        *reinterpret_cast<LT2*>(&s_k[buf][at]) = kx;
-        *reinterpret_cast<LT2*>(&s_v[buf][atv]) = vx;
+        *reinterpret_cast<u32x4*>(&s_k[buf][at]) = kx[0];
+        *reinterpret_cast<u32x4*>(&s_k[buf][at + 16]) = kx[1];
+        *reinterpret_cast<u32x4*>(&s_v[buf][atv]) = vx[0];
+        *reinterpret_cast<u32x4*>(&s_v[buf][atv + 16]) = vx[1];
       } else {
-        *reinterpret_cast<LT*>(&s_k[buf][at]) = kr[i];
+        *reinterpret_cast<u32x4*>(&s_k[buf][at]) = kr[j];
         if constexpr (KV == PA_BF16 && !FB) {
-          LT vx;
+          u32x4 vx;
 #pragma unroll
-          for (int w = 0; w < LB / 4; ++w) {
-            const float lo = __uint_as_float(vr[i][w] << 16);
-            const float hi = __uint_as_float(vr[i][w] & 0xffff0000u);
+          for (int w = 0; w < 4; ++w) {
+            const float lo = __uint_as_float(vr[j][w] << 16);
+            const float hi = __uint_as_float(vr[j][w] & 0xffff0000u);
             vmax = __builtin_elementwise_maximum(            // NaN-propagating
                 vmax, __builtin_elementwise_maximum(__builtin_fabsf(lo), __builtin_fabsf(hi)));
             vx[w] = pack_f16(lo, hi);
           }
-          *reinterpret_cast<LT*>(&s_v[buf][atv]) = vx;
+          *reinterpret_cast<u32x4*>(&s_v[buf][atv]) = vx;
         } else {
-          *reinterpret_cast<LT*>(&s_v[buf][atv]) = vr[i];
+          *reinterpret_cast<u32x4*>(&s_v[buf][atv]) = vr[j];
         }
       }
     }
+    if (lane == 0) reinterpret_cast<uint8_t*>(&s_bad[buf])[wave] = bad ? 1 : 0;
   };
 
   // ---- running state: row li's reference max m (log2 units; the running max, moved only
@@ -282,7 +283,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   f32x4 acc[RG][DPL], lsum[RG];
 
   // one key tile: scores, online softmax, P.V. MASKED: positions past a row's own, and the
-  // blocks flagged in `bad`, get weight 0. FB: V staged as bf16, p as hi + lo bf16 parts.
+  // blocks flagged in `bad` (byte s nonzero: block s of the tile lies outside the pool), get
+  // weight 0. FB: V staged as bf16, p as hi + lo bf16 parts.
   auto compute = [&](int buf, int kt, int bad, auto masked_tag, auto fb_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr bool FB = decltype(fb_tag)::value;
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           live[s][v] = !MASKED || (kt * kTileTokens + 16 * s + 4 * lk + v <= qpos[rg] &&
-                                   !((bad >> s) & 1));
+                                   !((bad >> (8 * s)) & 1));
           bm = fmaxf(bm, live[s][v] ? sc[rg][s][v] : neg_inf());
         }
       const float mx = xrow_max(fmaxf(bm * qks, m[rg]));   // the row's running max
@@ -417,32 +419,29 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[rg][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    u32x4 idv = {0u, 0u, 0u, 0u};
-    LT kr[4], vr[4];
-    int bad_next = 0;                      // bad blocks of the tile staged last
+    uint32_t id = 0;
+    u32x4 kr[NLD], vr[NLD];
+    bool bad = false;
     if (ntiles > 0) {
-      idv = load_ids(0);
-      bad_next = bad_blocks(0, idv);
-      stage(0, idv, kr, vr);
-      idv = load_ids(1);
-      to_lds(0, kr, vr, fb_tag);
+      id = load_id(0);
+      bad = stage(0, id, kr, vr);
+      id = load_id(1);
+      to_lds(0, kr, vr, bad, fb_tag);
     }
     __syncthreads();
     auto step = [&](int kt, auto masked_tag) {
       const bool more = kt + 1 < ntiles;
-      const int bad = bad_next;
       if (more) {
-        bad_next = bad_blocks(kt + 1, idv);
-        stage(kt + 1, idv, kr, vr);
-        idv = load_ids(kt + 2);
+        bad = stage(kt + 1, id, kr, vr);
+        id = load_id(kt + 2);
       }
-      compute(kt & 1, kt, bad, masked_tag, fb_tag);
-      if (more) to_lds((kt + 1) & 1, kr, vr, fb_tag);
+      compute(kt & 1, kt, (int)s_bad[kt & 1], masked_tag, fb_tag);
+      if (more) to_lds((kt + 1) & 1, kr, vr, bad, fb_tag);
       __syncthreads();
     };
     const int nfree = nfull < ntiles ? nfull : ntiles;
     int kt = 0;
-    for (; kt < nfree && bad_next == 0; ++kt) step(kt, std::false_type{});
+    for (; kt < nfree && s_bad[kt & 1] == 0; ++kt) step(kt, std::false_type{});
     for (; kt < ntiles; ++kt) step(kt, std::true_type{});
   };
   run(std::false_type{});
