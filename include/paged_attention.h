@@ -68,8 +68,10 @@ typedef enum {
  *                       (BF16,FP8_E4M3,BF16|F32)
  *   partition_size      0 (default): the KV work of the whole batch (16-token blocks of
  *                       every sequence and kv head) is cut into equal contiguous chunks,
- *                       one per workgroup of a fixed grid, whatever the length mix; a
- *                       sequence is cut only where a chunk ends. Otherwise a multiple of
+ *                       one per workgroup of a fixed grid (8 waves per compute unit; a
+ *                       smaller one, about two blocks per chunk, when the batch's
+ *                       blocks at max_context_len would not fill it), whatever the length
+ *                       mix; a sequence is cut only where a chunk ends. Otherwise a multiple of
  *                       16 (tokens), the split-KV partition: the work is cut into m equal
  *                       contiguous chunks per workgroup, m the smallest count for which no
  *                       chunk holds more than partition_size tokens of a sequence and kv

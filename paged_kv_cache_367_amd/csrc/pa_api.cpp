@@ -68,6 +68,20 @@ int num_workgroups(const pa_decode_desc_t* d) {
 // Units per chunk for an explicit partition size (0: default split).
 int part_units(const pa_decode_desc_t* d) { return d->partition_size / pa::kBlockTokens; }
 
+// Workgroups of this call's decode grid. Under the default split a call whose work is
+// small (at most segments * ceil(max_context_len / 16) units) takes about two units per
+// chunk rather than one chunk per workgroup of the device grid: half the pieces for the
+// merge to fold, for one more unit in each workgroup's pipeline (at least 32 workgroups).
+int decode_grid(const pa_decode_desc_t* d, int32_t max_context_len) {
+  const int W = num_workgroups(d);
+  if (part_units(d) > 0) return W;
+  const int64_t seq_blocks = ((int64_t)max_context_len + pa::kBlockTokens - 1) / pa::kBlockTokens;
+  const int64_t units =
+      (int64_t)(d->num_kv_heads / pa::group_waves(d->num_kv_heads)) * d->batch * seq_blocks;
+  const int64_t want = (units + 1) / 2;
+  return want >= W ? W : (int)(want > 32 ? want : 32);
+}
+
 // Most chunks a call can have, which sizes the records in the workspace: the W static
 // ones, plus with fixed partitions every partition of the largest possible unit count.
 int64_t max_chunks(const pa_decode_desc_t* d, int32_t max_context_len) {
@@ -210,7 +224,7 @@ pa_status_t decode_impl(const pa_decode_desc_t* desc, void* out, const void* q,
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
   char* wsb = static_cast<char*>(workspace);
   const int nw = pa::group_waves(desc->num_kv_heads);
-  const int W = num_workgroups(desc);
+  const int W = decode_grid(desc, max_context_len);
 
   pa::DecodeArgs a;
   a.out = out;
