@@ -44,8 +44,8 @@
 //     16 tokens get weight 0 in every row (from the first tile holding one, every tile
 //     takes the masked body).
 //   * Workgroup ids are dealt so that all query tiles of one (sequence, kv head) land on
-//     the same XCD (workgroups go to the 8 XCDs round-robin) and share its L2; within a
-//     pair, later tiles (longer key ranges) start first.
+//     the same XCD (workgroups go to the 8 XCDs round-robin) and share its L2; sequences
+//     go longest first, and within a pair, later tiles (longer key ranges) start first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -107,15 +107,34 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kTileTokens * VROW];
 
   // ---- which (sequence, kv head, query tile): id = ((group * tiles) + tile') * 8 + x,
-  // pair = group * 8 + x, tile = tiles - 1 - tile'
+  // pair = group * 8 + x, tile = tiles - 1 - tile'; pair p is kv head p % Hkv of the
+  // sequence ranked p / Hkv, sequences ranked longest first (ties by index) when the batch
+  // has at most one sequence per thread, else in index order. Workgroups start in id order,
+  // so the longest causal ranges start first and short ones fill the end of the launch.
   // (integer division runs on the vector ALU: uni() keeps the results scalar)
   const int id = blockIdx.x;
   const int x8 = id & 7, rest = id >> 3;
   const int grp = uni(rest / a.num_q_tiles);
   const int pair = grp * 8 + x8;
-  if (pair >= a.batch * a.num_kv_heads) return;
+  if (pair >= a.batch * a.num_kv_heads) return;   // (the whole workgroup)
   const int tile = a.num_q_tiles - 1 - (rest - grp * a.num_q_tiles);
-  const int b = uni(pair / a.num_kv_heads), kvh = pair - b * a.num_kv_heads;
+  const int rank = uni(pair / a.num_kv_heads), kvh = pair - rank * a.num_kv_heads;
+  int b = rank;
+  if (a.batch <= kPrefillThreads) {
+    __shared__ int s_len[kPrefillThreads];
+    __shared__ int s_seq;
+    const int t = threadIdx.x;
+    if (t < a.batch) s_len[t] = a.context_lens[t];
+    __syncthreads();
+    if (t < a.batch) {
+      const int Lt = s_len[t];
+      int r = 0;
+      for (int j = 0; j < a.batch; ++j) r += s_len[j] > Lt || (s_len[j] == Lt && j < t);
+      if (r == rank) s_seq = t;               // ranks are a permutation of [0, batch)
+    }
+    __syncthreads();
+    b = uni(s_seq);
+  }
   // the sequence's rows, kept inside [0, Tq) whatever query_start holds; rows past
   // max_query_len are not computed, though they still count in the positions
   const int Tq = a.num_query_tokens;
