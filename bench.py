@@ -22,7 +22,9 @@ against a read ceiling measured on the same GPU after the timed region (pa_strea
 over 4 GiB: the library's streaming-read kernel, the best a read-only kernel does here;
 a 1 GiB device copy, bytes read plus written, is reported beside it). With the default
 workload (3) the Llama-2-7B fp16, prefix-sharing and long-context fp8 workloads (2, 4, 5)
-are measured the same way afterwards and reported under `other_workloads`.
+are measured the same way afterwards and reported under `other_workloads`, one
+chunked-prefill step (see --path prefill, 20 timed steps) under `prefill`, and the tiny fp32
+workload's per-call GPU time from a HIP graph under `tiny_workload_latency`.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the main workload.
 
 With --path prefill the step is one chunked-prefill step instead (workload.chunked_prefill:
@@ -217,6 +219,14 @@ def prefill_cpu_baseline(w, gpu_out, budget_s: float):
 
 
 def run_prefill(args) -> int:
+    record = prefill_record(args, args.steps, args.warmup, not args.no_cpu_baseline)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def prefill_record(args, steps, warmup, with_cpu_baseline):
+    """One chunked-prefill step (slot write of the chunk's K/V, then pa_prefill) timed over
+    `steps` steps after `warmup` untimed ones; returns the JSON record."""
     import numpy as np
     import torch
 
@@ -257,8 +267,8 @@ def run_prefill(args) -> int:
     torch.cuda.synchronize()
     log(f"resident: {R} pool replicas")
     flops = prefill_flops(w)
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
 
     def step(i, timed):
         r = i % R
@@ -270,26 +280,26 @@ def run_prefill(args) -> int:
         if timed:
             ev1[i].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    log(f"warmup done ({warmup} steps)")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, True)
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = start.elapsed_time(end) / steps
     lms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
     lavg = sum(lms) / len(lms)
-    log(f"timed {args.steps} steps: {ms:.4f} ms/step, prefill launch avg {lavg:.4f} ms "
+    log(f"timed {steps} steps: {ms:.4f} ms/step, prefill launch avg {lavg:.4f} ms "
         f"(min {min(lms):.4f}, max {max(lms):.4f})")
     achieved = flops / (lavg * 1e-3) / 1e12
     record = {
         "metric": PREFILL_METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded, workload.py)",
         "config": {
@@ -311,13 +321,12 @@ def run_prefill(args) -> int:
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if with_cpu_baseline:
         log(f"cpu baseline: timing the oracle (~{args.cpu_budget_s:.0f} s)")
         gpu_out = out.to(torch.float64).cpu().numpy()
         record["cpu_baseline"] = prefill_cpu_baseline(w, gpu_out, args.cpu_budget_s)
         log(f"cpu baseline: {record['cpu_baseline']['sample']}")
-    print(json.dumps(record), flush=True)
-    return 0
+    return record
 
 
 PCIE_PEAK_GBS = 64.0        # PCIe 5.0 x16 host link, per direction
@@ -555,6 +564,17 @@ def main() -> int:
             del mx
             torch.cuda.empty_cache()
     if extra:
+        # the multi-token (chunked-prefill) step, fewer steps, no oracle timing
+        log("multi-token queries: one chunked-prefill step")
+        rp = prefill_record(args, min(args.steps, 20), 5, False)
+        record["prefill"] = {k: rp[k] for k in ("metric", "value", "unit", "ms_per_step",
+                                                "steps", "dtype")}
+        record["prefill"]["config"] = {k: rp["config"][k] for k in (
+            "workload", "batch", "query_tokens", "context_tokens", "flops_per_step")}
+        record["prefill"]["roofline"] = {k: rp["roofline"][k] for k in (
+            "kernel", "bound", "achieved", "peak", "unit", "frac", "traffic", "launch_ms")}
+        del rp
+        torch.cuda.empty_cache()
         # the tiny fp32 workload is latency-bound: GPU time per call from a HIP graph
         wt = wl.make(1)
         us, same = graph_latency(wt, 0)
