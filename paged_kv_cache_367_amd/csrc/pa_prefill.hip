@@ -220,9 +220,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const __amdgpu_buffer_rsrc_t rt =
       make_rsrc(a.block_tables + (size_t)b * a.max_blocks_per_seq, (uint32_t)nb * 4u);
   auto load_id = [&](int kt) -> uint32_t { return buf_load4(rt, (uint32_t)(kt * 4 + wave) * 4u); };
-  // K/V of wave w's block in tile kt into registers; returns whether the block lies below
-  // L with an id outside the pool (never read; its 16 tokens are masked out of the softmax)
-  auto stage = [&](int kt, uint32_t id, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) -> bool {
+  // K of wave w's block in tile kt into registers (its V descriptor kept for stage_v);
+  // returns whether the block lies below L with an id outside the pool (never read; its
+  // 16 tokens are masked out of the softmax). The V loads are issued later, after the
+  // tile's score MFMAs: the four waves of a workgroup reach the staging together after
+  // each barrier, and half of their loads then queue at the CU's address unit at once
+  // instead of all of them.
+  __amdgpu_buffer_rsrc_t rv_next = make_rsrc(vpool, 0u);
+  auto stage = [&](int kt, uint32_t id, u32x4 (&kr)[NLD]) -> bool {
     const int rem = L - (kt * 4 + wave) * kBlockTokens;   // rows of the block below L
     const uint32_t pid = (uint32_t)uni((int)id);
     const bool ok = rem > 0 && pid < (uint32_t)a.num_blocks;
@@ -231,13 +236,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     const uint32_t rows = (uint32_t)(rem < kBlockTokens ? rem : kBlockTokens);
     const uint32_t bytes = ok ? (rows - 1u) * tok_stride + ROWB : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, bytes);
+    rv_next = make_rsrc(vpool + base, bytes);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      kr[j] = buf_load16(rk, ld_off[j]);
-      vr[j] = buf_load16(rv, ld_off[j]);
-    }
+    for (int j = 0; j < NLD; ++j) kr[j] = buf_load16(rk, ld_off[j]);
     return rem > 0 && !ok;
+  };
+  auto stage_v = [&](u32x4 (&vr)[NLD]) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) vr[j] = buf_load16(rv_next, ld_off[j]);
   };
   // per LDS buffer, one byte per wave: its block of the tile staged there is out of pool
   __shared__ uint32_t s_bad[2];
@@ -301,10 +307,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   float m[RG];
   f32x4 acc[RG][DPL], lsum[RG];
 
-  // one key tile: scores, online softmax, P.V. MASKED: positions past a row's own, and the
+  // one key tile: scores, `after_scores` (once the score MFMAs are issued), online
+  // softmax, P.V. MASKED: positions past a row's own, and the
   // blocks flagged in `bad` (byte s nonzero: block s of the tile lies outside the pool), get
   // weight 0. FB: V staged as bf16, p as hi + lo bf16 parts.
-  auto compute = [&](int buf, int kt, int bad, auto masked_tag, auto fb_tag) {
+  auto compute = [&](int buf, int kt, int bad, auto masked_tag, auto fb_tag,
+                     auto&& after_scores) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr bool FB = decltype(fb_tag)::value;
     constexpr int PT = FB ? PA_BF16 : PA_F16;           // element type of the P.V MFMAs
@@ -326,6 +334,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         sc[rg][s] = z;
       }
     }
+    after_scores();
     u32x4 aop[RG][2];                      // P as the A operand, two subtiles per MFMA
     u32x4 alo[FB ? RG : 1][2];             // the low parts of P (FB)
 #pragma unroll
@@ -443,7 +452,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     bool bad = false;
     if (ntiles > 0) {
       id = load_id(0);
-      bad = stage(0, id, kr, vr);
+      bad = stage(0, id, kr);
+      stage_v(vr);
       id = load_id(1);
       to_lds(0, kr, vr, bad, fb_tag);
     }
@@ -451,10 +461,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     auto step = [&](int kt, auto masked_tag) {
       const bool more = kt + 1 < ntiles;
       if (more) {
-        bad = stage(kt + 1, id, kr, vr);
+        bad = stage(kt + 1, id, kr);
         id = load_id(kt + 2);
       }
-      compute(kt & 1, kt, (int)s_bad[kt & 1], masked_tag, fb_tag);
+      compute(kt & 1, kt, (int)s_bad[kt & 1], masked_tag, fb_tag, [&]() {
+        if (more) stage_v(vr);
+      });
       if (more) to_lds((kt + 1) & 1, kr, vr, bad, fb_tag);
       __syncthreads();
     };
