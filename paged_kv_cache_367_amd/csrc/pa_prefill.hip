@@ -33,7 +33,8 @@
 //     MFMAs (P times a column of ones), so that it sums exactly the rounded weights and
 //     the output stays an exact weighted average of V rows. bf16 V converts to fp16
 //     exactly below 2^16 in magnitude (values under 2^-17 move by less than 2^-25). Where
-//     a workgroup meets a bf16 V value of 2^16 or more (or an infinity or NaN) it runs its
+//     a workgroup meets a bf16 V value of 2^16 or more (or an infinity or NaN), which
+//     leaves a non-finite accumulator behind, it runs its
 //     key loop again with V staged as bf16 and p split into hi (p with its low 16 bits
 //     cleared, exact) and lo = bf16(p - hi), both taken by bf16 MFMAs (weights exact to
 //     about 2^-16, at twice the P.V matrix work). bf16 weights in one pass (rounding up
@@ -249,10 +250,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   __shared__ uint32_t s_bad[2];
   // V rows go to LDS as fp16 for the P.V matrix cores: fp16 and fp8 (exactly widened) as
   // they are, bf16 converted (exact for every |v| below 2^16, the tiniest values aside,
-  // which move by less than 2^-25). vmax tracks the largest |v| converted; a bf16 V
-  // value of 2^16 or more, an infinity or a NaN sends the workgroup through the pass again
-  // with V staged as bf16 and p split into two bf16 parts (FB).
-  float vmax = 0.0f;
+  // which move by less than 2^-25; a larger one becomes an infinity, and so does its
+  // product with any weight, or a NaN with a weight of 0: the accumulators are checked
+  // once at the end, see below).
   auto to_lds = [&](int buf, const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD], bool bad,
                     auto fb_tag) {
     constexpr bool FB = decltype(fb_tag)::value;
@@ -285,11 +285,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           u32x4 vx;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const float lo = __uint_as_float(vr[j][w] << 16);
-            const float hi = __uint_as_float(vr[j][w] & 0xffff0000u);
-            vmax = __builtin_elementwise_maximum(            // NaN-propagating
-                vmax, __builtin_elementwise_maximum(__builtin_fabsf(lo), __builtin_fabsf(hi)));
-            vx[w] = pack_f16(lo, hi);
+            vx[w] = pack_f16(__uint_as_float(vr[j][w] << 16),
+                             __uint_as_float(vr[j][w] & 0xffff0000u));
           }
           *reinterpret_cast<u32x4*>(&s_v[buf][atv]) = vx;
         } else {
@@ -476,8 +473,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     for (; kt < ntiles; ++kt) step(kt, std::true_type{});
   };
   run(std::false_type{});
+  // bf16 V: a value beyond fp16's range (2^16 or more, an infinity or a NaN) has left a
+  // non-finite accumulator in some row of the workgroup (its fp16 infinity times a weight,
+  // or times a zero weight of a masked position: NaN), while a finite V gives finite sums
+  // (weights at most 2^kLazyMax, |v| below 2^16). Such a workgroup runs its key loop again
+  // with V staged as bf16 and each weight split into two bf16 parts (FB), and stores only
+  // that result.
   if constexpr (KV == PA_BF16) {
-    if (__syncthreads_or(!(vmax < 65536.0f))) run(std::true_type{});
+    float amax = 0.0f;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(acc[rg][e][v]));  // NaN-propagating
+    if (__syncthreads_or(!(amax <= __FLT_MAX__))) run(std::true_type{});
   }
 
   // ---- normalise and store: lane (j, lk) writes rows 4lk + v, dims 16e + j
