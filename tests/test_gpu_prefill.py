@@ -217,3 +217,23 @@ def test_bf16_v_beyond_the_fp16_range():
         err = max_abs_err(got[rows], ref[rows])
         print(f"sequence {b}: max |v| {vm:.4g}, max_abs_err {err:.3e}", flush=True)
         assert err <= 2e-3 + 1e-4 * vm
+
+
+def test_more_sequences_than_threads_keeps_index_order():
+    """Sequences are dispatched longest first when the batch has at most one sequence per
+    thread of a workgroup (256); a larger batch (300 here, with ragged lengths, an empty
+    sequence and one whose queries are all its tokens) takes them in index order. Every row
+    against the oracle."""
+    rng = np.random.default_rng(23)
+    B = 300
+    n = rng.integers(0, 6, size=B)
+    L = n + rng.integers(0, 40, size=B)
+    n[:2] = [0, 4]
+    L[:2] = [0, 4]                          # empty, n = L
+    w = wl.prefill_custom(query_lens=n, context_lens=L, num_q_heads=8, num_kv_heads=2,
+                          head_dim=64, kv_dtype="bf16", out_dtype="f32", seed=23)
+    got = as_f64(_run(w, _device(w)))
+    ref = _oracle(w)
+    err = max_abs_err(got, ref)
+    print(f"B={B}: max_abs_err {err:.3e}", flush=True)
+    assert err <= 2e-3
