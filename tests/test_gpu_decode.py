@@ -155,35 +155,38 @@ def test_error_codes_on_device_buffers():
     assert e.value.status == -5
 
 
-@pytest.mark.parametrize("part", [0, 16])
-def test_out_of_pool_block_ids_are_masked(part):
+@pytest.mark.parametrize("part", [0, 16, 64])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_out_of_pool_block_ids_are_masked(kv, part):
     """A table entry below L that lies outside [0, num_blocks) is never dereferenced and
     its 16 tokens are left out of the softmax: the result equals the attention over the
     sequence's other tokens (attention does not depend on token order), and a sequence
-    whose blocks are all outside the pool gives zeros."""
+    whose blocks are all outside the pool gives zeros; bf16 and fp8 K/V, the default split
+    and two partition sizes."""
     import dataclasses
     lens = [100, 40, 64, 17]
-    w = wl.custom(batch=4, num_q_heads=16, num_kv_heads=4, head_dim=128, kv_dtype="bf16",
+    w = wl.custom(batch=4, num_q_heads=16, num_kv_heads=4, head_dim=128, kv_dtype=kv,
                   context_lens=lens, seed=21)
     N = w.num_blocks
     bad = w.block_tables.copy()
     bad[0, 2] = N + 5          # a full block in the middle
     bad[1, 0] = -7             # the first block
+    bad[2, 3] = N + 1          # the last block
     bad[3, :2] = [N, 2 ** 31 - 1]   # every block of the sequence
     # the same attention written with valid tables: the bad blocks' tokens removed
     good = np.full_like(bad, -1)
     good[0, :6] = np.delete(w.block_tables[0, :7], 2)
     good[1, :2] = w.block_tables[1, 1:3]
-    good[2] = w.block_tables[2]
+    good[2, :3] = w.block_tables[2, :3]
     exp = dataclasses.replace(w, block_tables=good,
-                              context_lens=np.array([84, 24, 64, 0], dtype=np.int32))
+                              context_lens=np.array([84, 24, 48, 0], dtype=np.int32))
     ref = oracle_decode(exp)
     w_bad = dataclasses.replace(w, block_tables=bad)
     out = as_f64(gpu_decode(w_bad, to_device(w_bad), partition_size=part, out_dtype="f32"))
     assert (out[3] == 0).all()
     err = max_abs_err(out, ref)
-    print(f"out-of-pool ids, partition {part}: max_abs_err={err:.3e}", flush=True)
-    assert err <= FP32_OUT_TOL["bf16"]
+    print(f"out-of-pool ids, {kv}, partition {part}: max_abs_err={err:.3e}", flush=True)
+    assert err <= FP32_OUT_TOL[kv]
 
 
 @pytest.mark.parametrize("part", [0, 256])
