@@ -33,7 +33,8 @@
 //     contraction takes the 16-bit hi part and the 16-bit lo part of every weight p against
 //     the same V row, so the weights enter within 2^-16 of their fp32 value; l sums the
 //     fp32 weights. Lane (n, kq) loads dims D/16*n .. of tokens 4kq .. 4kq+3; the B operand
-//     is two byte permutes away.
+//     is two byte permutes away (fp8: one byte permute per two dims interleaves two tokens
+//     before the conversions, which then give B operand halves directly).
 //   * fp32 K/V: QK^T on v_mfma_f32_16x16x4f32, p through LDS, and P.V on the vector ALU in
 //     fp32: lane (r, c) owns V chunk c of rows r, r + RPI, ... for all G heads; lanes
 //     owning the same chunk are summed at the end of a piece.
@@ -123,22 +124,13 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Matrix-core P.V (16-bit and fp8 K/V). V words of one token row, as pairs of 16-bit values
-// in the MFMA's element type (fp8 widened exactly to bf16).
+// Matrix-core P.V (16-bit K/V). V words of one token row, as pairs of 16-bit values in the
+// MFMA's element type.
 template <int KV, int WORDS, typename VTy>
 __device__ __forceinline__ void v_words16(const VTy& w, uint32_t (&o)[WORDS]) {
-  if constexpr (KV == PA_FP8_E4M3) {
+  static_assert(KV == PA_F16 || KV == PA_BF16, "16-bit V");
 #pragma unroll
-    for (int i = 0; i < WORDS / 2; ++i) {
-      o[2 * i] = __builtin_bit_cast(uint32_t,
-                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-      o[2 * i + 1] = __builtin_bit_cast(uint32_t,
-                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) o[i] = w[i];
-  }
+  for (int i = 0; i < WORDS; ++i) o[i] = w[i];
 }
 // Matrix-core path: scores as K.Q^T, so that the MFMA's output layout (lane (n, kq): rows
 // 4kq + v, column n) gives each lane tokens 4kq .. 4kq+3 of head n % G, which is the A
@@ -557,6 +549,12 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   float acc[G][VEPC];                      // vector-ALU P.V: lane (r, c), all G heads
   float m1 = 0.0f, l1 = 0.0f;              // matrix-core path: head n % G, partial l
   float qks = a.qk_scale_log2;             // score scale of the piece's kv head (log2 units)
+  // matrix-core path: the softmax takes the max of the raw scores and folds the scale into
+  // the exponent's fma, which needs a scale >= 0; a negative one is moved onto q (an exact
+  // sign flip of its 16-bit elements). At least the smallest normal float, so that a
+  // masked score of -inf times it stays -inf (finite scores times it round to equal
+  // weights, as with a zero scale).
+  float qka = 0.0f;
   f32x4 acc4[DPL];                         // matrix-core P.V: dim DPL*n + e, rows 4kq + v
   bool piece_whole_start = false;          // the current piece began at its segment's start
   int piece_slot = 0;
@@ -603,6 +601,16 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       piece_slot = (fl & kAtStart) ? 0 : 1;
       // per-head dequantisation: kv head g's K codes times k_head_scales[g]
       if constexpr (PH) qks = (a.qk_scale * a.k_head_scales[g]) * kLog2e;
+      if constexpr (MPV) {
+        static_assert(QB == 2, "16-bit q on the matrix-core path");
+        qka = fmaxf(fabsf(qks), __FLT_MIN__);
+        if (qks < 0.0f) {
+#pragma unroll
+          for (int s2 = 0; s2 < NL; ++s2)
+#pragma unroll
+            for (int u = 0; u < QCH; ++u) qreg[s2][u] ^= 0x80008000u;
+        }
+      }
     }
     const int rem = mu.rem();              // tokens of this block below L
     const bool ragged = rem < kBlockTokens;
@@ -612,23 +620,25 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NL; ++s) sc = kq_chunk<KV>(sc, kb[s], qreg[s]);
+      // raw scores (tokens at or past L: -inf); the max commutes with the non-negative
+      // scale, rounding included
       float sv[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sv[v] = sc[v] * qks;
+        sv[v] = sc[v];
         if (ragged) sv[v] = 4 * kq + v < rem ? sv[v] : neg_inf();
       }
       // new running max of head n % G: over the lane's 4 tokens and the running max, then
       // over the 4 row groups, which hold the block's other tokens
       const float b01 = sv[0] > sv[1] ? sv[0] : sv[1], b23 = sv[2] > sv[3] ? sv[2] : sv[3];
-      const float bm = b01 > b23 ? b01 : b23;
+      const float bm = (b01 > b23 ? b01 : b23) * qka;
       const float mn = xrow_max(bm > m1 ? bm : m1);
       const float al1 = mn == neg_inf() ? 1.0f : fast_exp2(m1 - mn);
       // (mn is -inf only while every token so far was masked: then every p is 0)
       const float mref = mn == neg_inf() ? 0.0f : mn;
       float pf[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) pf[v] = fast_exp2(sv[v] - mref);   // 0 for masked tokens
+      for (int v = 0; v < 4; ++v) pf[v] = fast_exp2(fmaf(sv[v], qka, -mref));   // 0 if masked
       // the matrix cores take p in 16 bits, as a hi and a lo part (within 2^-16 of p)
       const u32x4 aop = split_pack4<KV>(pf);
       l1 = l1 * al1 + ((pf[0] + pf[1]) + (pf[2] + pf[3]));
@@ -652,16 +662,41 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
           for (int v = 0; v < 4; ++v) acc4[e][v] *= alv[v];
       }
       // B operands: token rows 4kq + i of this lane's dims (rows at or past L read as zero)
-      constexpr int WORDS = DPL / 2;
-      uint32_t vw[4][WORDS];
+      if constexpr (KV == PA_FP8_E4M3) {
+        // fp8: interleave the bytes of tokens 2p and 2p + 1 first (one byte permute per two
+        // dims), so that each conversion yields the bf16 pair (token 2p, token 2p + 1) of
+        // one dim, which is a half of the B operand as it is
+        uint32_t pw[2][DPL];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v_words16<KV, WORDS>(vb[i], vw[i]);
+        for (int pr = 0; pr < 2; ++pr)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x2 bop = {__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
-                           __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel)};
-        acc4[e] = mfma_pv<KV>(aop, bop, acc4[e]);
+          for (int w = 0; w < DPL / 4; ++w) {
+            const uint32_t a = vb[2 * pr][w], b = vb[2 * pr + 1][w];
+            const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+            const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+            pw[pr][4 * w] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+            pw[pr][4 * w + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+            pw[pr][4 * w + 2] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+            pw[pr][4 * w + 3] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+          }
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc4[e] = mfma_pv<KV>(aop, u32x2{pw[0][e], pw[1][e]}, acc4[e]);
+      } else {
+        constexpr int WORDS = DPL / 2;
+        uint32_t vw[4][WORDS];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v_words16<KV, WORDS>(vb[i], vw[i]);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const u32x2 bop = {__builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel),
+                             __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel)};
+          acc4[e] = mfma_pv<KV>(aop, bop, acc4[e]);
+        }
       }
     } else {
       // vector-ALU P.V (fp32 K/V). Scores of token t = lane % 16 for the heads of MFMA rows

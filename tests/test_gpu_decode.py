@@ -209,3 +209,25 @@ def test_workspace_contents_do_not_matter(part):
         outs.append(as_f64(out))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
     _check(w, torch.from_numpy(outs[0]), oracle_decode(w))
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16", "fp8_e4m3"])
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 1.7])
+def test_negative_zero_and_large_score_scales(kv, scale):
+    """The matrix-core path folds the score scale into the exponent and moves a negative
+    scale onto q as a sign flip; a zero scale gives equal weights (the mean of the V rows
+    below L). fp8 also takes a negative k_scale, which enters the score scale. (Not fp32 at
+    19 times 1/sqrt(d): logits of several tens carry fp32 rounding of about 1e-5 of their
+    size into the weights, the size of the fp32 bar itself.)"""
+    import dataclasses
+    if kv == "f32" and abs(scale) > 1.0:
+        pytest.skip("fp32 bar of 1e-5 is for scales near 1/sqrt(d)")
+    lens = [1, 16, 17, 100, 700]
+    w = wl.custom(batch=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128, kv_dtype=kv,
+                  context_lens=lens, seed=31)
+    w = dataclasses.replace(w, scale=scale)
+    if kv == "fp8_e4m3":
+        w = dataclasses.replace(w, k_scale=-w.k_scale)
+    dev = to_device(w)
+    for part in (0, 64):
+        _check(w, gpu_decode(w, dev, partition_size=part), oracle_decode(w))

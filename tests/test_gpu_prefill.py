@@ -237,3 +237,15 @@ def test_more_sequences_than_threads_keeps_index_order():
     err = max_abs_err(got, ref)
     print(f"B={B}: max_abs_err {err:.3e}", flush=True)
     assert err <= 2e-3
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_negative_and_zero_score_scales(kv, scale):
+    """A negative score scale (moved onto q as a sign flip) and a zero one (equal weights
+    over each row's causal range) against the oracle."""
+    import dataclasses
+    w = wl.prefill_custom(query_lens=[1, 20, 70], context_lens=[9, 20, 150], num_q_heads=8,
+                          num_kv_heads=2, head_dim=128, kv_dtype=kv, seed=7)
+    w = dataclasses.replace(w, scale=scale)
+    _check(w, _run(w, _device(w)), _oracle(w))
