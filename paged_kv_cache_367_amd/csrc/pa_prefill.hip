@@ -16,7 +16,9 @@
 //     global loads of the next tile are in flight while the current one is computed. K
 //     rows reach LDS in the score type (bf16 for bf16 and fp8 K, fp16 for fp16; fp8
 //     widened exactly), V rows in fp16 (fp8 widened exactly, bf16 converted: see below).
-//     K rows are padded by 16 bytes and V rows by 32 to spread the banks.
+//     16-bit K goes from HBM straight into LDS (buffer loads with the lds bit), requested
+//     after the tile's score MFMAs, its rows unpadded with the 16-byte chunks XOR-swizzled
+//     by row; fp8 K rows are padded by 16 bytes, V rows by 32, to spread the banks.
 //   * The P.V operand B (eight consecutive tokens of one output dim) comes straight from
 //     the row-major V tile through transposed LDS reads (ds_read_b64_tr_b16), so MFMA e
 //     covers output dims 16e + n; no byte permutes.
@@ -83,6 +85,13 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 acc) {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l
+// writes lds + 16 l; a lane whose offset is out of range writes zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
 // Two floats rounded to fp16 / bf16 (nearest even) and packed, a in the low half.
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
@@ -96,7 +105,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr int ST = KV == PA_F16 ? PA_F16 : PA_BF16;  // element type of the score MFMAs
   constexpr int KB = Enc<KV>::bytes;
   constexpr int ROWB = D * KB;                   // pool bytes of one token row, one kv head
-  constexpr int LROW = D * 2 + kKPad;            // LDS bytes of one K token row (16-bit)
+  // 16-bit K goes from HBM straight into LDS (KDMA): rows unpadded, the 16-byte chunks of
+  // row r stored at chunk ^ (r mod the chunks per row), which spreads the banks as the pad
+  // does; fp8 K is widened in registers on its way and keeps the padded rows
+  constexpr bool KDMA = KB == 2;
+  constexpr int LROW = KDMA ? D * 2 : D * 2 + kKPad;   // LDS bytes of one K token row (16-bit)
   constexpr int VROW = D * 2 + kVPad;            // LDS bytes of one V token row (16-bit)
   constexpr int ROWS = kPrefillWaves * RG * 16;  // (token, head) rows of the workgroup
   constexpr int TQ = ROWS / G;                   // query tokens of the workgroup
@@ -214,6 +227,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
   for (int j = 0; j < NLD; ++j)
     ld_off[j] = (uint32_t)(j * RPL + lane / TPC) * tok_stride + (uint32_t)(lane % TPC) * 16u;
+  // KDMA: lane l of load j writes LDS row j * RPL + l / TPC, slot l % TPC, so it fetches the
+  // chunk that the swizzle puts there
+  uint32_t ldk_off[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int row = j * RPL + lane / TPC;
+    ldk_off[j] = (uint32_t)row * tok_stride + (uint32_t)((lane % TPC) ^ (row & (TPC - 1))) * 16u;
+  }
   // the block id of wave w's block in tile kt (table entry 4kt + w, the same for every lane
   // of the wave), loaded one tile ahead with the K/V prefetch of the tile before, so its
   // wait is the one the K/V data already takes; entries at or past nb read as 0 and are
@@ -221,8 +242,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const __amdgpu_buffer_rsrc_t rt =
       make_rsrc(a.block_tables + (size_t)b * a.max_blocks_per_seq, (uint32_t)nb * 4u);
   auto load_id = [&](int kt) -> uint32_t { return buf_load4(rt, (uint32_t)(kt * 4 + wave) * 4u); };
-  // K of wave w's block in tile kt into registers (its V descriptor kept for stage_v);
-  // returns whether the block lies below L with an id outside the pool (never read; its
+  // K of wave w's block in tile kt into registers, or for 16-bit K straight into LDS
+  // buffer kt & 1 (its V descriptor kept for stage_v); returns whether the block lies below L with an id outside the pool (never read; its
   // 16 tokens are masked out of the softmax). The V loads are issued later, after the
   // tile's score MFMAs: the four waves of a workgroup reach the staging together after
   // each barrier, and half of their loads then queue at the CU's address unit at once
@@ -238,8 +259,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     const uint32_t bytes = ok ? (rows - 1u) * tok_stride + ROWB : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, bytes);
     rv_next = make_rsrc(vpool + base, bytes);
+    if constexpr (KDMA) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) kr[j] = buf_load16(rk, ld_off[j]);
+      for (int j = 0; j < NLD; ++j)
+        buf_load16_lds(rk, &s_k[kt & 1][(kBlockTokens * wave + j * RPL) * LROW], ldk_off[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) kr[j] = buf_load16(rk, ld_off[j]);
+    }
     return rem > 0 && !ok;
   };
   auto stage_v = [&](u32x4 (&vr)[NLD]) {
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         *reinterpret_cast<u32x4*>(&s_v[buf][atv]) = vx[0];
         *reinterpret_cast<u32x4*>(&s_v[buf][atv + 16]) = vx[1];
       } else {
-        *reinterpret_cast<u32x4*>(&s_k[buf][at]) = kr[j];
+        if constexpr (!KDMA) *reinterpret_cast<u32x4*>(&s_k[buf][at]) = kr[j];
         if constexpr (KV == PA_BF16 && !FB) {
           u32x4 vx;
 #pragma unroll
@@ -322,7 +349,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       u32x4 kop[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kop[c] = *reinterpret_cast<const u32x4*>(Kt + (16 * s + li) * LROW + (32 * c + 8 * lk) * 2);
+        kop[c] = *reinterpret_cast<const u32x4*>(
+            Kt + (16 * s + li) * LROW +
+            (KDMA ? ((4 * c + lk) ^ (li & (TPC - 1))) * 16 : (32 * c + 8 * lk) * 2));
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
         f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -454,17 +483,28 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       id = load_id(1);
       to_lds(0, kr, vr, bad, fb_tag);
     }
+    if constexpr (KDMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K landed in LDS
     __syncthreads();
     auto step = [&](int kt, auto masked_tag) {
       const bool more = kt + 1 < ntiles;
-      if (more) {
+      // (KDMA: the next tile's K is requested after this tile's score MFMAs, so that it
+      // lands in LDS while the softmax and P.V run rather than under the score phase's
+      // operand reads)
+      if (more && !KDMA) {
         bad = stage(kt + 1, id, kr);
         id = load_id(kt + 2);
       }
       compute(kt & 1, kt, (int)s_bad[kt & 1], masked_tag, fb_tag, [&]() {
-        if (more) stage_v(vr);
+        if (more) {
+          if constexpr (KDMA) {
+            bad = stage(kt + 1, id, kr);
+            id = load_id(kt + 2);
+          }
+          stage_v(vr);
+        }
       });
       if (more) to_lds((kt + 1) & 1, kr, vr, bad, fb_tag);
+      if constexpr (KDMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K landed in LDS
       __syncthreads();
     };
     const int nfree = nfull < ntiles ? nfull : ntiles;
