@@ -23,7 +23,11 @@
 //   * 16-bit and fp8 K/V: scores are computed as K.Q^T on the matrix cores
 //     (v_mfma_f32_16x16x32_{bf16,f16}; fp8 is widened exactly to bf16 first). Operand A
 //     is the K block exactly as it sits in HBM: lane (t, q) = (lane % 16, lane / 16) loads
-//     16-byte chunk 4s+q of token t's row. Operand B repeats the G query rows over the 16
+//     16-byte chunk 4s+q of token t's row. fp8 K, whose row of one kv head is a single
+//     128-byte line, goes through LDS instead: loads that each take whole rows (8 lanes per
+//     row) write a per-slot LDS ring directly (buffer loads with the lds bit, chunks
+//     XOR-swizzled by row), and each unit's operand is read back from there one unit
+//     ahead; half-line loads cost the fp8 path 3%. Operand B repeats the G query rows over the 16
 //     MFMA columns (column n holds head n % G), laid out once per piece through LDS. The
 //     MFMA's output leaves lane (n, kq) with the scores of tokens 4kq .. 4kq+3 for head
 //     n % G, which is the A-operand layout of P in P.V, so P never leaves registers.
@@ -131,6 +135,12 @@ __device__ __forceinline__ void v_words16(const VTy& w, uint32_t (&o)[WORDS]) {
   static_assert(KV == PA_F16 || KV == PA_BF16, "16-bit V");
 #pragma unroll
   for (int i = 0; i < WORDS; ++i) o[i] = w[i];
+}
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l
+// writes lds + 16 l; a lane whose offset is out of range writes zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
 }
 // Matrix-core path: scores as K.Q^T, so that the MFMA's output layout (lane (n, kq): rows
 // 4kq + v, column n) gives each lane tokens 4kq .. 4kq+3 of head n % G, which is the A
@@ -315,6 +325,14 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ int s_wsum[kMaxGroupWaves];
   __shared__ float s_p[kMaxGroupWaves][2 * PBUF];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[kMaxGroupWaves][QBYTES];
+  // fp8 K (KLDS): each ring slot's K blocks, one per wave, loaded whole token rows at a
+  // time straight into LDS and read back in the matrix-core operand layout; one array per
+  // slot, so that reading a slot waits only for that slot's loads
+  constexpr bool KLDS = KV == PA_FP8_E4M3;
+  constexpr int KBLK = kBlockTokens * ROWB;            // K bytes of one block, one kv head
+  constexpr int KR_BYTES = KLDS ? kMaxGroupWaves * KBLK : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t s_kr0[KR_BYTES], s_kr1[KR_BYTES],
+      s_kr2[KR_BYTES], s_kr3[KR_BYTES];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int nthr = blockDim.x;
@@ -503,6 +521,25 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   const uint8_t* const qbase = static_cast<const uint8_t*>(a.q);
   // per-lane byte offsets inside one kv head's slice of a block (constant)
   const uint32_t koff = (lane & 15) * tok_stride + (lane >> 4) * 16;
+  // KLDS: load s of a block takes token rows TPI*s .. TPI*s + TPI - 1 whole (LPT lanes per
+  // row); lane l writes LDS row l / LPT, slot l % LPT, and so fetches the 16-byte chunk the
+  // swizzle (chunk ^ (row mod LPT)) stores there
+  constexpr int LPT = ROWB / 16 < kWave ? ROWB / 16 : kWave;   // lanes per K token row
+  constexpr int TPI = kWave / LPT;                             // token rows per load
+  const uint32_t kdma_off = (uint32_t)(lane / LPT) * tok_stride +
+                            (uint32_t)((lane % LPT) ^ ((lane / LPT) & (LPT - 1))) * 16u;
+  auto kslot = [&](int u) -> uint8_t* {
+    return (u == 0 ? s_kr0 : (u == 1 ? s_kr1 : (u == 2 ? s_kr2 : s_kr3))) + wave * KBLK;
+  };
+  // KLDS: the K operand of the unit in ring slot u, back from LDS in the layout of the
+  // matrix-core loads (lane (t, q) = (lane % 16, lane / 16): chunk 4s + q of token t)
+  auto kload = [&](u32x4(&kc)[NL], int u) {
+    const int t = lane & 15;
+    const uint8_t* kr = kslot(u) + t * ROWB;
+#pragma unroll
+    for (int s = 0; s < NL; ++s)
+      kc[s] = *reinterpret_cast<const u32x4*>(kr + (((4 * s + (lane >> 4)) ^ (t & (LPT - 1))) * 16));
+  };
   const uint32_t voff = MPV ? (4 * (lane >> 4)) * tok_stride + (lane & 15) * VB
                             : (lane / LPR) * tok_stride + (lane % LPR) * VB;
   const uint32_t vstep = MPV ? tok_stride : RPI * tok_stride;   // between a lane's V loads
@@ -520,7 +557,7 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
   // A block id outside [0, num_blocks) is never dereferenced: its unit keeps rem = 0, so
   // all 16 of its tokens are masked out of the softmax like rows past L.
   auto issue = [&](auto pol, UnitMeta& m, uint32_t idv, u32x4(&kb)[NL], VT(&vb)[NLV],
-                   u32x4(&qs)[QPL]) {
+                   u32x4(&qs)[QPL], int slot) {
     constexpr int POL = decltype(pol)::value;
     const int pid = __builtin_amdgcn_readfirstlane((int)idv);
     const bool valid = (m.flags() & kValid) && (unsigned)pid < (unsigned)a.num_blocks;
@@ -537,8 +574,15 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < QPL; ++i) qs[i] = buf_load16(rq, (uint32_t)(lane + kWave * i) * 16u);
     // K and V with the workgroup's cache policy (streaming unless blocks are shared)
+    if constexpr (KLDS) {
+      static_assert(TPI * NL == kBlockTokens && NBUF + 1 <= 4, "K ring in LDS");
 #pragma unroll
-    for (int s = 0; s < NL; ++s) kb[s] = buf_load16<POL>(rk, koff + s * 64);
+      for (int s = 0; s < NL; ++s)
+        buf_load16_lds(rk, kslot(slot) + s * TPI * ROWB, kdma_off + (uint32_t)(s * TPI) * tok_stride);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NL; ++s) kb[s] = buf_load16<POL>(rk, koff + s * 64);
+    }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) vb[i] = VChunk<VB>::template load<POL>(rv, voff + i * vstep);
   };
@@ -876,11 +920,13 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       mk[u] = mi[u];
-      issue(pol, mk[u], idv[u], kb[u], vb[u], qs[u]);
+      issue(pol, mk[u], idv[u], kb[u], vb[u], qs[u], u);
       mi[u] = snapshot();
       idv[u] = load_id(mi[u]);
       advance();
     }
+    u32x4 kcur[NL];
+    if constexpr (KLDS) kload(kcur, 0);
     if (!cg.fixed && wave == 0 && lane == 0) {
       int4 hd = make_int4(-1, 0, 0, 0);
       if (hdr_b >= 0) {
@@ -895,11 +941,18 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       for (int u = 0; u < R; ++u) {
         const int si = (u + NBUF) % R;   // slot of unit k + NBUF (= slot of unit k - 1)
         mk[si] = mi[si];
-        issue(pol, mk[si], idv[si], kb[si], vb[si], qs[si]);
+        issue(pol, mk[si], idv[si], kb[si], vb[si], qs[si], si);
         mi[si] = snapshot();
         idv[si] = load_id(mi[si]);
         advance();
-        compute(mk[u], kb[u], vb[u], qs[u], pw + (u & 1) * PBUF);
+        if constexpr (KLDS) {
+          // K of unit k came back from LDS during step k - 1; unit k + 1's is read now,
+          // after unit k's matrix-core work is issued
+          compute(mk[u], kcur, vb[u], qs[u], pw + (u & 1) * PBUF);
+          kload(kcur, (u + 1) % R);
+        } else {
+          compute(mk[u], kb[u], vb[u], qs[u], pw + (u & 1) * PBUF);
+        }
       }
       bool busy = cur >= 0;
 #pragma unroll
