@@ -231,3 +231,15 @@ def test_negative_zero_and_large_score_scales(kv, scale):
     dev = to_device(w)
     for part in (0, 64):
         _check(w, gpu_decode(w, dev, partition_size=part), oracle_decode(w))
+
+
+@pytest.mark.parametrize("kv,part", [("bf16", 0), ("fp8_e4m3", 0), ("fp8_e4m3", 64)])
+def test_largest_batch(kv, part):
+    """4096 sequences, the most a call takes (their lengths and prefix sums fill LDS), with
+    lengths 0..40 (empty, one-block and two-block sequences side by side); every output
+    against the oracle."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 41, size=4096)
+    w = wl.custom(batch=4096, num_q_heads=8, num_kv_heads=2, head_dim=128, kv_dtype=kv,
+                  context_lens=lens, seed=77)
+    _check(w, gpu_decode(w, to_device(w), partition_size=part), oracle_decode(w))
