@@ -1068,9 +1068,9 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int i = 0; i < EPL; ++i) A[i] = 0.0f;
   for (int kb = wave; kb < np; kb += MW * UNROLL) {
-    // every load is issued (a piece past the last reads piece 0's record and is dropped).
-    // One unit per chunk: lane u works out the chunk of piece kb + u MW, so the round's
-    // divisions run side by side, and each load reads its chunk from that lane.
+    // the round's loads are issued together and stop at the last piece. One unit per
+    // chunk: lane u works out the chunk of piece kb + u MW, so the round's divisions run
+    // side by side, and each load reads its chunk from that lane.
     int cl = 0;
     if (by_unit) {
       const int kk = kb + (lane % UNROLL) * MW;
@@ -1080,8 +1080,9 @@ __global__ __launch_bounds__(1024) void merge_kernel(MergeArgs a) {
     float x[UNROLL][EPL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int k = kb + u * MW, kq = k < np ? k : 0;
-      const size_t rec = rec_of(by_unit ? __builtin_amdgcn_readlane(cl, u) : cf + kq, kq);
+      const int k = kb + u * MW;
+      if (k >= np) break;   // (the same in the whole wave)
+      const size_t rec = rec_of(by_unit ? __builtin_amdgcn_readlane(cl, u) : cf + k, k);
       mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
       load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
     }
@@ -1190,9 +1191,9 @@ __global__ __launch_bounds__(kMaxThreads) void merge_chunk_kernel(MergeArgs a) {
     const int u0 = Ts > 0 ? Ts * cf / W : 0;             // the segment's first unit
     const int n = Ts > 0 ? Ts * c / W - u0 : c - cf;     // pieces before chunk c
     for (int kb = 0; kb < n; kb += UNROLL) {
-      // every load is issued (a piece past the last reads chunk c's own record), so
-      // the UNROLL pieces cost one round trip; those past the last are dropped. One unit
-      // per chunk: lane u works out the chunk of piece kb + u (divisions side by side).
+      // the round's loads are issued together (one round trip for up to UNROLL pieces)
+      // and stop at the last piece. One unit per chunk: lane u works out the chunk of
+      // piece kb + u (divisions side by side).
       int cl = c;
       if (Ts > 0) {
         const int kk = kb + lane % UNROLL;
@@ -1203,7 +1204,8 @@ __global__ __launch_bounds__(kMaxThreads) void merge_chunk_kernel(MergeArgs a) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int k = kb + u;
-        const int cc = Ts > 0 ? __builtin_amdgcn_readlane(cl, u) : (k >= n ? c : cf + k);
+        if (k >= n) break;   // (the same in the whole wave)
+        const int cc = Ts > 0 ? __builtin_amdgcn_readlane(cl, u) : cf + k;
         const size_t rec = rec_of(cc, (k == 0) ? slot_f : 0);
         mlp[u] = *reinterpret_cast<const f32x2*>(a.rec_ml + rec * 2);
         load_floats<EPL>(a.rec_acc + rec * D + d0, x[u]);
