@@ -668,15 +668,20 @@ __global__ __launch_bounds__(kMaxThreads, 1) void decode_kernel(DecodeArgs a) {
       // scale, rounding included
       float sv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sv[v] = sc[v];
-        if (ragged) sv[v] = 4 * kq + v < rem ? sv[v] : neg_inf();
+      for (int v = 0; v < 4; ++v) sv[v] = sc[v];
+      // only a sequence's last block is ragged: a branch on the (uniform) flag, kept as one
+      // by the empty asm, which the compiler cannot turn into selects run on every unit
+      if (ragged) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          sv[v] = 4 * kq + v < rem ? sv[v] : neg_inf();
+          asm volatile("" : "+v"(sv[v]));
+        }
       }
       // new running max of head n % G: over the lane's 4 tokens and the running max, then
       // over the 4 row groups, which hold the block's other tokens
-      const float b01 = sv[0] > sv[1] ? sv[0] : sv[1], b23 = sv[2] > sv[3] ? sv[2] : sv[3];
-      const float bm = (b01 > b23 ? b01 : b23) * qka;
-      const float mn = xrow_max(bm > m1 ? bm : m1);
+      const float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) * qka;
+      const float mn = xrow_max(fmaxf(bm, m1));
       const float al1 = mn == neg_inf() ? 1.0f : fast_exp2(m1 - mn);
       // (mn is -inf only while every token so far was masked: then every p is 0)
       const float mref = mn == neg_inf() ? 0.0f : mn;
