@@ -385,7 +385,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int v = 0; v < 4; ++v) sv[s][v] = fmaf(sc[rg][s][v], qks, -base);
-      const float al = m[rg] == mn ? 1.0f : fast_exp2(m[rg] - base);
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi) {
         uint32_t w[4], wl[4];
@@ -411,9 +410,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         aop[rg][pi] = u32x4{w[0], w[1], w[2], w[3]};
         if constexpr (FB) alo[rg][pi] = u32x4{wl[0], wl[1], wl[2], wl[3]};
       }
+      const float mold = m[rg];
       m[rg] = mn;
-      // rows 4lk + v of the accumulators take the factor of row 4lk + v (held by lane 4lk + v)
-      if (__builtin_amdgcn_ballot_w64(al != 1.0f) != 0) {
+      // rows 4lk + v of the accumulators take the factor of row 4lk + v (held by lane 4lk + v),
+      // worked out only when some row's reference moved
+      if (__builtin_amdgcn_ballot_w64(mn != mold) != 0) {
+        const float al = mn == mold ? 1.0f : fast_exp2(mold - base);
         float alv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) alv[v] = __shfl(al, 4 * lk + v);
