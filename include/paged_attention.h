@@ -20,7 +20,9 @@
  *     only. Contents of device arrays (table entries, lengths, slots, pairs) are the
  *     caller's contract: kernels never read or write outside the pool for out-of-range
  *     entries (they skip them), but the result for such entries is unspecified.
- *   - No global mutable state: calls are thread-safe.
+ *   - No global mutable state, so calls are thread-safe; the one exception is the static
+ *     per-GPU scratch of pa_decode_noalloc, whose calls must not overlap on one GPU (see
+ *     there).
  */
 #ifndef PAGED_ATTENTION_H
 #define PAGED_ATTENTION_H
