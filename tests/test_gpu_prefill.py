@@ -249,3 +249,52 @@ def test_negative_and_zero_score_scales(kv, scale):
                           num_kv_heads=2, head_dim=128, kv_dtype=kv, seed=7)
     w = dataclasses.replace(w, scale=scale)
     _check(w, _run(w, _device(w)), _oracle(w))
+
+
+def _reference_moves(w, tile=64, lazy=8.0):
+    """Rows whose running reference max moves after their first key tile, replaying in fp64
+    the rule the kernel follows: the reference (log2 units) moves to the running max only
+    when that max outgrows it by more than `lazy`, checked once per `tile` positions."""
+    from oracle.storage import decode_storage
+    q = decode_storage(w.q, w.q_dtype)
+    k = decode_storage(w.k_pool, w.kv_dtype) * w.k_scale
+    G = w.num_q_heads // w.num_kv_heads
+    moved = 0
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        r0, r1 = int(w.query_start[b]), int(w.query_start[b + 1])
+        n = r1 - r0
+        ids = w.block_tables[b, :(L + 15) // 16]
+        keys = k[ids].reshape(-1, *k.shape[2:])[:L]          # [L, Hkv, d]
+        for i in range(n):
+            pos = L - n + i
+            for h in range(w.num_q_heads):
+                s = keys[:pos + 1, h // G] @ q[r0 + i, h] * w.scale / np.log(2.0)
+                ref = -np.inf
+                for t0 in range(0, pos + 1, tile):
+                    mx = max(ref, s[t0:t0 + tile].max())
+                    if mx > ref + lazy:
+                        moved += t0 > 0
+                        ref = mx
+    return moved
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("scale", [1.5, 4.0])
+def test_large_score_scales_move_the_reference_max(kv, scale):
+    """Score scales far above 1/sqrt(d) spread the logits over tens of log2 units, so the
+    running max of many rows outgrows its reference by more than 2^8 after the first key
+    tile: the accumulators are then rescaled mid-row, not only at the first tile where
+    they are still zero. For bf16 the number of such mid-row moves is replayed on the host
+    and must be positive. fp32 output, so only the kernel's rounding is left: bound 2e-3,
+    as with the scale of 1/sqrt(d)."""
+    import dataclasses
+    w = wl.prefill_custom(query_lens=[3, 40, 130], context_lens=[700, 300, 1100],
+                          num_q_heads=8, num_kv_heads=2, head_dim=128, kv_dtype=kv,
+                          out_dtype="f32", seed=31)
+    w = dataclasses.replace(w, scale=scale)
+    if kv == "bf16":
+        moves = _reference_moves(w)
+        print(f"scale {scale}: {moves} mid-row reference moves", flush=True)
+        assert moves > 0
+    _check(w, _run(w, _device(w)), _oracle(w), tol=2e-3)
